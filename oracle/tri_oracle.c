@@ -1,0 +1,194 @@
+/*
+ * tri_oracle.c -- CPU ORACLE for the ternary linear layer.  TEST INFRASTRUCTURE ONLY.
+ *
+ * This is the plain, slow, obviously-correct reference that the HIP library is
+ * checked against.  It is not part of the product: only the test suite, the
+ * smoke check and the CPU-baseline leg of the benchmark load it.  It shares no
+ * source, header, table or helper with the HIP library, and the HIP library never
+ * loads it.
+ *
+ * What it follows (the web pages on Spectra 1.1, arXiv 2506.23025):
+ *   [PR] "Pith review of Spectra 1.1: Scaling Laws and Efficient Inference for
+ *        Ternary Language Models" (pith.science):
+ *        - "What carries the argument": a ternary linear layer has a weight matrix
+ *          in {-1,0,1} times one shared floating-point scale; k trits fit
+ *          losslessly in p bits when 2^p > 3^k, so k=5 trits fit in p=8 bits
+ *          (1.6 bits per weight).
+ *        - "Core claim": lossless 2-bit packing by base-4 encoding and 1.6-bit
+ *          packing by base-3 encoding.
+ *        - "Referee Report", minor comment 5 (paper section 3.2): the 1.6-bit
+ *          decode is written as a sequence b'_i -> x_i; the final partial block is
+ *          not specified.
+ *        - "Significance": the packing correctness theorem (paper Appendix E),
+ *          i.e. unpacking a packed block returns the block.
+ *   [SP] "Spectra 1.1: Scaling Laws and Efficient Inference for Ternary Language
+ *        Models" (shd-paper.top summary), abstract: 2-bit and 1.6-bit packing of
+ *        ternary weights.
+ *
+ * Readings taken where the pages are silent (stated once here, used below):
+ *   - digit of a trit t is d = t + 1 in {0,1,2} (non-negative base-4 / base-3 digits);
+ *   - the lowest k index is the least-significant digit of its byte;
+ *   - a row of K trits is padded with zero trits (d = 1) to a multiple of 64 trits
+ *     (2-bit, 16 bytes) or 80 trits (1.6-bit, 16 bytes); rows are stored one after
+ *     another, output row n first (out x in, like nn.Linear);
+ *   - packing encodes sign(w), so any int8 input is accepted;
+ *   - unpack is defined for every byte value: 2-bit code 3 gives 0; 1.6-bit bytes
+ *     243..255 go through the same repeated division by 3;
+ *   - the layer returns scale * sum_k t[n][k] * x[m][k] exactly as summed in
+ *     float64 in k order, unrounded.
+ *
+ * Build: gcc -O2 -fopenmp -shared -fPIC tri_oracle.c -o liboracle.so
+ */
+#include <stdint.h>
+#include <stddef.h>
+#include <math.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { OR_FMT_2BIT = 0, OR_FMT_1P6BIT = 1 };
+
+/* Bytes of one packed row: 16*ceil(K/64) for 2-bit, 16*ceil(K/80) for 1.6-bit; -1 if invalid. */
+int64_t oracle_row_bytes(int64_t K, int fmt)
+{
+    if (K < 1) return -1;
+    if (fmt == OR_FMT_2BIT) return 16 * ((K + 63) / 64);
+    if (fmt == OR_FMT_1P6BIT) return 16 * ((K + 79) / 80);
+    return -1;
+}
+
+/* Digit of weight w: sign(w) + 1. */
+static int digit_of(int8_t w)
+{
+    if (w > 0) return 2;
+    if (w < 0) return 0;
+    return 1;
+}
+
+/* Trit k of row n, zero beyond the end of the row. */
+static int8_t trit_at(const int8_t *W, int64_t K, int64_t n, int64_t k)
+{
+    if (k >= K) return 0;
+    return W[n * K + k];
+}
+
+/* 2-bit packing, base-4 encoding ([PR] "Core claim"):
+ * byte b of row n = sum_{j=0..3} d(4b+j) * 4^j. */
+void oracle_pack2(const int8_t *W, int64_t N, int64_t K, uint8_t *Wp)
+{
+    int64_t S = oracle_row_bytes(K, OR_FMT_2BIT);
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t b = 0; b < S; ++b) {
+            int value = 0;
+            int power = 1;
+            for (int j = 0; j < 4; ++j) {
+                value += digit_of(trit_at(W, K, n, 4 * b + j)) * power;
+                power *= 4;
+            }
+            Wp[n * S + b] = (uint8_t)value;
+        }
+    }
+}
+
+/* 1.6-bit packing, base-3 encoding of 5 trits per byte, possible because
+ * 3^5 = 243 < 2^8 ([PR] "What carries the argument", "Core claim"):
+ * byte b of row n = sum_{j=0..4} d(5b+j) * 3^j, evaluated by Horner's rule. */
+void oracle_pack16(const int8_t *W, int64_t N, int64_t K, uint8_t *Wp)
+{
+    int64_t S = oracle_row_bytes(K, OR_FMT_1P6BIT);
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t b = 0; b < S; ++b) {
+            int value = 0;
+            for (int j = 4; j >= 0; --j)
+                value = value * 3 + digit_of(trit_at(W, K, n, 5 * b + j));
+            Wp[n * S + b] = (uint8_t)value;
+        }
+    }
+}
+
+/* Unpack (inverse of the two packings; [PR] "Significance", Appendix E theorem;
+ * "Referee Report" minor comment 5 for the b'_i -> x_i iteration).
+ * Writes the first K trits of every row. Returns 0, or -1 on an unknown format. */
+int oracle_unpack(const uint8_t *Wp, int64_t N, int64_t K, int fmt, int8_t *W)
+{
+    int64_t S = oracle_row_bytes(K, fmt);
+    if (S < 0) return -1;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t b = 0; b < S; ++b) {
+            int byte = Wp[n * S + b];
+            if (fmt == OR_FMT_2BIT) {
+                for (int j = 0; j < 4; ++j) {
+                    int64_t k = 4 * b + j;
+                    int code = (byte >> (2 * j)) & 3;
+                    int t = (code == 3) ? 0 : code - 1;
+                    if (k < K) W[n * K + k] = (int8_t)t;
+                }
+            } else {
+                int rest = byte;                 /* b'_0 */
+                for (int j = 0; j < 5; ++j) {
+                    int x = rest % 3;            /* x_j = b'_j mod 3 */
+                    rest = rest / 3;             /* b'_{j+1} = floor(b'_j / 3) */
+                    int64_t k = 5 * b + j;
+                    if (k < K) W[n * K + k] = (int8_t)(x - 1);
+                }
+            }
+        }
+    }
+    return 0;
+}
+
+/* IEEE 754 binary16 bit pattern -> double (exact). */
+double oracle_half_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int exponent = (h >> 10) & 0x1f;
+    int mantissa = h & 0x3ff;
+    double v;
+    if (exponent == 0)
+        v = ldexp((double)mantissa, -24);               /* subnormal or zero */
+    else if (exponent == 31)
+        v = mantissa ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + mantissa), exponent - 25);
+    return sign ? -v : v;
+}
+
+/* The ternary linear layer ([PR] "What carries the argument"):
+ *   Y[m][n] = scale * sum_{k<K} t[n][k] * x[m][k]
+ * X holds M*K fp16 bit patterns (row-major), W holds N*K trits (row-major),
+ * Y receives M*N float64 values, unrounded.  Sums run over k in order, in float64.
+ * Returns 0, or -1 if X holds a non-finite value (the layer is defined on finite
+ * activations only).  nthreads > 0 sets the OpenMP thread count (output rows are
+ * split between threads; each element keeps its own k order, so the result does
+ * not depend on it). */
+int oracle_linear_f64(const uint16_t *X, const int8_t *W, double scale,
+                      int64_t M, int64_t N, int64_t K, double *Y, int nthreads)
+{
+    for (int64_t i = 0; i < M * K; ++i)
+        if (!isfinite(oracle_half_to_double(X[i]))) return -1;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    for (int64_t m = 0; m < M; ++m) {
+        #pragma omp parallel for schedule(static)
+        for (int64_t n = 0; n < N; ++n) {
+            double sum = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                sum += (double)W[n * K + k] * oracle_half_to_double(X[m * K + k]);
+            Y[m * N + n] = scale * sum;
+        }
+    }
+    return 0;
+}
+
+/* Number of OpenMP threads a parallel region would use (1 without OpenMP). */
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
