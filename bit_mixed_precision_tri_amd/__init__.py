@@ -1,0 +1,162 @@
+"""Python binding of libtri, the gfx950 ternary linear layer.
+
+The functions named ``tri_*`` mirror the C ABI in ``include/tri.h`` one to one:
+they only marshal arguments (device pointers of torch tensors, the current HIP
+stream) and raise ``TriError`` on a negative status.  All the work runs in the
+library's HIP kernels; there is no fallback of any kind -- if ``libtri.so`` is
+missing, every call raises.  The helpers at the end (``pack``, ``unpack``,
+``linear``) allocate their outputs with torch and then call the same entry points.
+"""
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "_lib", "libtri.so")
+
+TRI_FMT_2BIT = 0
+TRI_FMT_1P6BIT = 1
+TRI_OK, TRI_EINVAL, TRI_EALIGN, TRI_EHIP = 0, -1, -2, -3
+TRI_ALGO_AUTO, TRI_ALGO_GEMV, TRI_ALGO_SMALLM, TRI_ALGO_GEMM = 0, 1, 2, 3
+ALGO_NAMES = {TRI_ALGO_GEMV: "gemv", TRI_ALGO_SMALLM: "smallm", TRI_ALGO_GEMM: "gemm"}
+
+_lib = None
+
+
+class TriError(RuntimeError):
+    def __init__(self, code, what):
+        super().__init__("%s failed: %s (%d)" % (what, status_string(code), code))
+        self.code = code
+
+
+def lib():
+    """The loaded libtri.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libtri.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        i64, p, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        L.tri_row_bytes.argtypes = [i64, i32]
+        L.tri_row_bytes.restype = i64
+        for name in ("tri_pack2", "tri_pack16"):
+            getattr(L, name).argtypes = [p, i64, i64, p, p]
+            getattr(L, name).restype = i32
+        L.tri_unpack.argtypes = [p, i64, i64, i32, p, p]
+        L.tri_unpack.restype = i32
+        L.tri_linear.argtypes = [p, p, ctypes.c_float, i64, i64, i64, i32, p, p]
+        L.tri_linear.restype = i32
+        L.tri_linear_algo.argtypes = [p, p, ctypes.c_float, i64, i64, i64, i32, p, i32, p]
+        L.tri_linear_algo.restype = i32
+        L.tri_select_algo.argtypes = [i64, i64, i64, i32]
+        L.tri_select_algo.restype = i32
+        L.tri_status_string.argtypes = [i32]
+        L.tri_status_string.restype = ctypes.c_char_p
+        L.tri_probe_read.argtypes = [p, i64, p, p]
+        L.tri_probe_read.restype = i32
+        L.tri_probe_copy.argtypes = [p, p, i64, p]
+        L.tri_probe_copy.restype = i32
+        _lib = L
+    return _lib
+
+
+def status_string(code):
+    return lib().tri_status_string(int(code)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr() if hasattr(t, "data_ptr") else int(t))
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _check(rc, what):
+    if rc != TRI_OK:
+        raise TriError(rc, what)
+    return rc
+
+
+# ---------------------------------------------------------------- the C ABI, one to one
+
+def tri_row_bytes(K, fmt):
+    return int(lib().tri_row_bytes(int(K), int(fmt)))
+
+
+def tri_pack2(W, N, K, Wp, stream=None):
+    return _check(lib().tri_pack2(_ptr(W), int(N), int(K), _ptr(Wp), _stream(stream)), "tri_pack2")
+
+
+def tri_pack16(W, N, K, Wp, stream=None):
+    return _check(lib().tri_pack16(_ptr(W), int(N), int(K), _ptr(Wp), _stream(stream)), "tri_pack16")
+
+
+def tri_unpack(Wp, N, K, fmt, W, stream=None):
+    return _check(lib().tri_unpack(_ptr(Wp), int(N), int(K), int(fmt), _ptr(W), _stream(stream)), "tri_unpack")
+
+
+def tri_linear(X, Wp, scale, M, N, K, fmt, Y, stream=None):
+    return _check(lib().tri_linear(_ptr(X), _ptr(Wp), float(scale), int(M), int(N), int(K), int(fmt), _ptr(Y),
+                                   _stream(stream)), "tri_linear")
+
+
+def tri_linear_algo(X, Wp, scale, M, N, K, fmt, Y, algo, stream=None):
+    return _check(lib().tri_linear_algo(_ptr(X), _ptr(Wp), float(scale), int(M), int(N), int(K), int(fmt), _ptr(Y),
+                                        int(algo), _stream(stream)), "tri_linear_algo")
+
+
+def tri_select_algo(M, N, K, fmt):
+    return int(lib().tri_select_algo(int(M), int(N), int(K), int(fmt)))
+
+
+def tri_status_string(code):
+    return status_string(code)
+
+
+def tri_probe_read(src, nbytes, sink, stream=None):
+    return _check(lib().tri_probe_read(_ptr(src), int(nbytes), _ptr(sink), _stream(stream)), "tri_probe_read")
+
+
+def tri_probe_copy(src, dst, nbytes, stream=None):
+    return _check(lib().tri_probe_copy(_ptr(src), _ptr(dst), int(nbytes), _stream(stream)), "tri_probe_copy")
+
+
+# ---------------------------------------------------------------- allocating helpers
+
+def pack(W, fmt, stream=None):
+    """Pack a (N, K) int8 CUDA tensor; returns a new (N, row_bytes) uint8 tensor."""
+    import torch
+    N, K = W.shape
+    assert W.dtype == torch.int8 and W.is_cuda and W.is_contiguous()
+    Wp = torch.empty((N, tri_row_bytes(K, fmt)), dtype=torch.uint8, device=W.device)
+    (tri_pack2 if fmt == TRI_FMT_2BIT else tri_pack16)(W, N, K, Wp, stream)
+    return Wp
+
+
+def unpack(Wp, K, fmt, stream=None):
+    """Unpack a (N, row_bytes) uint8 CUDA tensor; returns a new (N, K) int8 tensor."""
+    import torch
+    N = Wp.shape[0]
+    assert Wp.dtype == torch.uint8 and Wp.is_cuda and Wp.is_contiguous()
+    assert Wp.shape[1] == tri_row_bytes(K, fmt)
+    W = torch.empty((N, K), dtype=torch.int8, device=Wp.device)
+    tri_unpack(Wp, N, K, fmt, W, stream)
+    return W
+
+
+def linear(X, Wp, scale, K, fmt, algo=TRI_ALGO_AUTO, out=None, stream=None):
+    """Y = fp16(scale * X @ W.T) for a (M, K) fp16 CUDA tensor X and packed weights Wp."""
+    import torch
+    M = X.shape[0]
+    N = Wp.shape[0]
+    assert X.dtype == torch.float16 and X.is_cuda and X.is_contiguous() and X.shape[1] == K
+    assert Wp.dtype == torch.uint8 and Wp.is_contiguous() and Wp.shape[1] == tri_row_bytes(K, fmt)
+    Y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=X.device)
+    if algo == TRI_ALGO_AUTO:
+        tri_linear(X, Wp, scale, M, N, K, fmt, Y, stream)
+    else:
+        tri_linear_algo(X, Wp, scale, M, N, K, fmt, Y, algo, stream)
+    return Y

@@ -1,0 +1,126 @@
+// tri_api.hip -- the extern "C" entry points of libtri: argument checks and dispatch.
+// Every check runs on the host before any launch; see include/tri.h for the contract.
+#include "tri_internal.h"
+
+using namespace tri;
+
+namespace {
+
+bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+bool known_fmt(int fmt) { return fmt == TRI_FMT_2BIT || fmt == TRI_FMT_1P6BIT; }
+constexpr int64_t kMaxDim = (int64_t)1 << 31;   // K, N and one packed row are indexed with 32-bit ints
+
+int check_pack(const void *W, int64_t N, int64_t K, const void *Wp)
+{
+    if (!W || !Wp || N < 1 || K < 1 || N >= kMaxDim || K >= kMaxDim) return TRI_EINVAL;
+    if (misaligned(Wp)) return TRI_EALIGN;
+    return TRI_OK;
+}
+
+int check_linear(const void *X, const void *Wp, int64_t M, int64_t N, int64_t K, int fmt, const void *Y)
+{
+    if (!X || !Wp || !Y || M < 1 || N < 1 || K < 1 || !known_fmt(fmt)) return TRI_EINVAL;
+    if (N >= kMaxDim || K >= kMaxDim || M >= kMaxDim) return TRI_EINVAL;
+    if (misaligned(X) || misaligned(Wp) || misaligned(Y)) return TRI_EALIGN;
+    return TRI_OK;
+}
+
+int select_algo(int64_t M, int fmt)
+{
+    if (M == 1 && fmt == TRI_FMT_2BIT) return TRI_ALGO_GEMV;
+    if (M <= 16) return TRI_ALGO_SMALLM;
+    return TRI_ALGO_GEMM;
+}
+
+int run_linear(const _Float16 *X, const uint8_t *Wp, float scale, int64_t M, int64_t N, int64_t K, int fmt,
+               _Float16 *Y, int algo, hipStream_t s)
+{
+    const uint16_t *x = reinterpret_cast<const uint16_t *>(X);
+    uint16_t *y = reinterpret_cast<uint16_t *>(Y);
+    switch (algo) {
+    case TRI_ALGO_GEMV:
+        if (M != 1 || fmt != TRI_FMT_2BIT) return TRI_EINVAL;
+        return launch_gemv2(x, Wp, scale, (int)N, (int)K, y, s);
+    case TRI_ALGO_SMALLM:
+        if (M > 16) return TRI_EINVAL;
+        return launch_smallm(x, Wp, scale, (int)M, (int)N, (int)K, fmt, y, s);
+    case TRI_ALGO_GEMM:
+        return launch_gemm(x, Wp, scale, M, (int)N, (int)K, fmt, y, s);
+    default:
+        return TRI_EINVAL;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t tri_row_bytes(int64_t K, int fmt) { return row_bytes(K, fmt); }
+
+int tri_pack2(const int8_t *W, int64_t N, int64_t K, uint8_t *Wp, hipStream_t stream)
+{
+    const int rc = check_pack(W, N, K, Wp);
+    return rc != TRI_OK ? rc : launch_pack(W, N, K, TRI_FMT_2BIT, Wp, stream);
+}
+
+int tri_pack16(const int8_t *W, int64_t N, int64_t K, uint8_t *Wp, hipStream_t stream)
+{
+    const int rc = check_pack(W, N, K, Wp);
+    return rc != TRI_OK ? rc : launch_pack(W, N, K, TRI_FMT_1P6BIT, Wp, stream);
+}
+
+int tri_unpack(const uint8_t *Wp, int64_t N, int64_t K, int fmt, int8_t *W, hipStream_t stream)
+{
+    if (!known_fmt(fmt)) return TRI_EINVAL;
+    const int rc = check_pack(W, N, K, Wp);
+    return rc != TRI_OK ? rc : launch_unpack(Wp, N, K, fmt, W, stream);
+}
+
+int tri_select_algo(int64_t M, int64_t N, int64_t K, int fmt)
+{
+    if (M < 1 || N < 1 || K < 1 || !known_fmt(fmt) || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return TRI_EINVAL;
+    return select_algo(M, fmt);
+}
+
+int tri_linear(const _Float16 *X, const uint8_t *Wp, float scale, int64_t M, int64_t N, int64_t K, int fmt,
+               _Float16 *Y, hipStream_t stream)
+{
+    const int rc = check_linear(X, Wp, M, N, K, fmt, Y);
+    return rc != TRI_OK ? rc : run_linear(X, Wp, scale, M, N, K, fmt, Y, select_algo(M, fmt), stream);
+}
+
+int tri_linear_algo(const _Float16 *X, const uint8_t *Wp, float scale, int64_t M, int64_t N, int64_t K, int fmt,
+                    _Float16 *Y, int algo, hipStream_t stream)
+{
+    const int rc = check_linear(X, Wp, M, N, K, fmt, Y);
+    if (rc != TRI_OK) return rc;
+    if (algo == TRI_ALGO_AUTO) algo = select_algo(M, fmt);
+    return run_linear(X, Wp, scale, M, N, K, fmt, Y, algo, stream);
+}
+
+const char *tri_status_string(int code)
+{
+    switch (code) {
+    case TRI_OK: return "ok";
+    case TRI_EINVAL: return "invalid argument";
+    case TRI_EALIGN: return "pointer not 16-byte aligned";
+    case TRI_EHIP: return "HIP launch error";
+    default: return "unknown status";
+    }
+}
+
+int tri_probe_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t stream)
+{
+    if (!src || !sink || bytes < 16 || (bytes % 16) != 0) return TRI_EINVAL;
+    if (misaligned(src)) return TRI_EALIGN;
+    return launch_probe_read(src, bytes, sink, stream);
+}
+
+int tri_probe_copy(const void *src, void *dst, int64_t bytes, hipStream_t stream)
+{
+    if (!src || !dst || bytes < 16 || (bytes % 16) != 0) return TRI_EINVAL;
+    if (misaligned(src) || misaligned(dst)) return TRI_EALIGN;
+    return launch_probe_copy(src, dst, bytes, stream);
+}
+
+}  // extern "C"

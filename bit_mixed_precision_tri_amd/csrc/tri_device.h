@@ -1,0 +1,138 @@
+// tri_device.h -- device-side helpers shared by the libtri kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tri {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// Two fp16 lanes of a 32-bit register.
+__device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
+
+// v_dot2_f32_f16: c + a.lo*b.lo + a.hi*b.hi with fp32 accumulation.  fp16 subnormal
+// inputs are honoured (verified on gfx950), which the trit decoders below rely on.
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2(as_h2(a), as_h2(b), c, false);
+}
+
+// v_perm_b32: byte i of the result is byte sel_i of the 8-byte value {hi:lo}.
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
+{
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// fp16 lane `e` (0 = low half, 1 = high half) of `lo` and lane `e` of `hi`, packed as (lo, hi).
+template <int E>
+__device__ __forceinline__ uint32_t pair_halves(uint32_t hi, uint32_t lo)
+{
+    return perm(hi, lo, E == 0 ? 0x05040100u : 0x07060302u);
+}
+
+// 16-byte global load.
+__device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+// NH consecutive fp16 values x[k0 .. k0+NH) of one activation row, as NH/2 registers
+// (x[2q], x[2q+1]); zero beyond K.  `vec` says the row start is 16-byte aligned.
+template <int NH>
+__device__ __forceinline__ void load_x_span(const uint16_t *__restrict__ xrow, int k0, int K, bool vec,
+                                            uint32_t (&out)[NH / 2])
+{
+    static_assert(NH % 8 == 0, "span must be whole 16-byte pieces");
+    if (vec && k0 + NH <= K) {
+#pragma unroll
+        for (int q = 0; q < NH / 8; ++q) {
+            uint4 v = ld16(xrow + k0 + 8 * q);
+            out[4 * q + 0] = v.x; out[4 * q + 1] = v.y; out[4 * q + 2] = v.z; out[4 * q + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < NH / 2; ++q) {
+            int k = k0 + 2 * q;
+            uint32_t lo = (k < K) ? xrow[k] : 0u;
+            uint32_t hi = (k + 1 < K) ? xrow[k + 1] : 0u;
+            out[q] = lo | (hi << 16);
+        }
+    }
+}
+
+// Cross-lane moves of gfx950 used by the wave reductions.
+// permlane32_swap(a, b): the upper 32 lanes of `a` trade places with the lower 32 lanes of `b`.
+__device__ __forceinline__ void swap32(float &a, float &b)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+// permlane16_swap(a, b): the odd 16-lane rows of `a` trade places with the even rows of `b`.
+__device__ __forceinline__ void swap16(float &a, float &b)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum RB (1, 2, 4 or 8) per-lane values over the 64 lanes of a wave, without LDS.  The
+// first steps trade halves of the value list between partner lanes (32 apart, then 16
+// apart, then mirrored inside a 16-lane row), so each lane keeps adding only the values of
+// its own half; the rest is a butterfly inside the row over the lane masks 15
+// (row_mirror), 7 (row_half_mirror), 2 and 1 (quad_perm).  The masks 32, 16, 15, 7, 2, 1
+// span all six lane bits.  Afterwards every lane of group r = lane >> (6 - log2(RB)) holds
+// the total of value r.  The order of the additions is fixed: results are deterministic.
+template <int RB>
+__device__ __forceinline__ float wave_reduce_rows(float (&v)[RB], int lane)
+{
+    static_assert(RB == 1 || RB == 2 || RB == 4 || RB == 8, "RB must be 1, 2, 4 or 8");
+    float s;
+    if constexpr (RB == 1) {
+        float a = v[0], b = v[0];
+        swap32(a, b);
+        s = a + b;
+        a = s;
+        b = s;
+        swap16(a, b);
+        s = a + b;
+    } else {
+#pragma unroll
+        for (int i = 0; i < RB / 2; ++i) {
+            swap32(v[i], v[i + RB / 2]);
+            v[i] += v[i + RB / 2];
+        }
+        if constexpr (RB == 2) {
+            float a = v[0], b = v[0];
+            swap16(a, b);
+            s = a + b;
+        } else {
+#pragma unroll
+            for (int i = 0; i < RB / 4; ++i) {
+                swap16(v[i], v[i + RB / 4]);
+                v[i] += v[i + RB / 4];
+            }
+            s = v[0];
+            if constexpr (RB == 8) {
+                const bool up = (lane & 8) != 0;
+                const float send = up ? v[0] : v[1];
+                const float keep = up ? v[1] : v[0];
+                s = keep + dpp<0x140>(send);
+            }
+        }
+    }
+    if constexpr (RB <= 4) s += dpp<0x140>(s);   // row_mirror: lane ^ 15 within a row
+    s += dpp<0x141>(s);                          // row_half_mirror: lane ^ 7 within 8 lanes
+    s += dpp<0x4E>(s);                           // quad_perm [2,3,0,1]: lane ^ 2
+    s += dpp<0xB1>(s);                           // quad_perm [1,0,3,2]: lane ^ 1
+    return s;
+}
+
+}  // namespace tri

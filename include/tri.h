@@ -1,0 +1,124 @@
+/*
+ * tri.h -- C ABI of libtri, the gfx950 (MI355X) ternary linear layer.
+ *
+ * The layer (Pith review of "Spectra 1.1: Scaling Laws and Efficient Inference
+ * for Ternary Language Models", section "What carries the argument"): a weight
+ * matrix W with entries in {-1, 0, +1} times one shared floating-point scale,
+ * applied to fp16 activations,
+ *
+ *     Y[m][n] = fp16_rne( scale * sum_k W[n][k] * X[m][k] ),   accumulated in fp32.
+ *
+ * Weights are stored losslessly in one of two packings (same review, "Core
+ * claim" and "What carries the argument": 2^p > 3^k, so 5 trits fit in 8 bits):
+ *
+ *   TRI_FMT_2BIT    base-4: byte = sum_{j<4} (t[4b+j] + 1) * 4^j
+ *                   (trit 4b+j in bits 2j..2j+1; digit 3 never produced)
+ *   TRI_FMT_1P6BIT  base-3: byte = sum_{j<5} (t[5b+j] + 1) * 3^j   (0..242)
+ *
+ * Layout of a packed matrix: N rows (output features) one after another, each
+ * tri_row_bytes(K, fmt) bytes long; a row is padded with zero trits to a
+ * multiple of 64 trits (2-bit) or 80 trits (1.6-bit), so every row is a whole
+ * number of 16-byte chunks and starts 16-byte aligned.
+ *
+ * Conventions for every call:
+ *  - All array pointers are DEVICE pointers owned by the caller.  The library
+ *    allocates no memory and keeps no mutable global state; calls are
+ *    thread-safe and deterministic (no atomics; the reduction order is fixed).
+ *  - Work is enqueued asynchronously on `stream` (0 = the null stream).  A
+ *    device fault surfaces at the caller's next synchronisation.
+ *  - Argument checks run on the host before anything is launched; on failure
+ *    nothing is launched and a negative status is returned.
+ *  - Outputs must not alias inputs.
+ */
+#ifndef TRI_H
+#define TRI_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { TRI_FMT_2BIT = 0, TRI_FMT_1P6BIT = 1 };
+
+enum {
+    TRI_OK = 0,
+    TRI_EINVAL = -1,   /* a size < 1 (or too large), a null pointer, an unknown format or algorithm */
+    TRI_EALIGN = -2,   /* a pointer that must be 16-byte aligned is not */
+    TRI_EHIP = -3      /* the HIP runtime reported an error at launch */
+};
+
+/* Kernel families of tri_linear (see tri_linear_algo). */
+enum {
+    TRI_ALGO_AUTO = 0,     /* pick from (M, fmt): the default of tri_linear */
+    TRI_ALGO_GEMV = 1,     /* M == 1, 2-bit only: VALU dot products, lanes own K-slices */
+    TRI_ALGO_SMALLM = 2,   /* 1 <= M <= 16: MFMA 16x16x32 f16 with trits decoded in registers */
+    TRI_ALGO_GEMM = 3      /* any M: tiled MFMA GEMM, trits decoded into LDS (prefill) */
+};
+
+/* Bytes of one packed row: 16*ceil(K/64) (2-bit) or 16*ceil(K/80) (1.6-bit).
+ * Returns -1 if K < 1 or fmt is unknown. */
+int64_t tri_row_bytes(int64_t K, int fmt);
+
+/* 2-bit packing (Pith review, "Core claim": base-4 encoding).
+ * W: N*K int8, row-major (row n = output feature n).  Any int8 is accepted and
+ * sign(w) is encoded.  Wp: N*tri_row_bytes(K, TRI_FMT_2BIT) bytes, 16-byte aligned.
+ * Errors: TRI_EINVAL (N < 1, K < 1, null), TRI_EALIGN (Wp), TRI_EHIP. */
+int tri_pack2(const int8_t *W, int64_t N, int64_t K, uint8_t *Wp, hipStream_t stream);
+
+/* 1.6-bit packing (Pith review, "What carries the argument": 3^5 = 243 < 2^8,
+ * 1.6 bits per weight; "Core claim": base-3 encoding).  Same arguments as
+ * tri_pack2 with rows of tri_row_bytes(K, TRI_FMT_1P6BIT) bytes. */
+int tri_pack16(const int8_t *W, int64_t N, int64_t K, uint8_t *Wp, hipStream_t stream);
+
+/* Unpack (Pith review, "Significance": the packing correctness theorem of the
+ * paper's Appendix E; "Referee Report" minor comment 5: the 1.6-bit decode is
+ * the repeated-division sequence b'_i -> x_i).  Defined for every byte value:
+ * a 2-bit code 3 gives 0, and 1.6-bit bytes 243..255 go through the same
+ * repeated division by 3 (five digits).  Writes the first K trits of each row.
+ * Wp: N rows of tri_row_bytes(K, fmt) bytes, 16-byte aligned; W: N*K int8.
+ * Errors: TRI_EINVAL, TRI_EALIGN (Wp), TRI_EHIP. */
+int tri_unpack(const uint8_t *Wp, int64_t N, int64_t K, int fmt, int8_t *W, hipStream_t stream);
+
+/* The ternary linear layer (Pith review, "What carries the argument"):
+ *   Y[m][n] = fp16_rne(scale * sum_k t[n][k] * X[m][k]), fp32 accumulation.
+ * X: M*K fp16 row-major (row stride K); Wp: packed weights as above; Y: M*N fp16
+ * row-major.  X, Wp and Y must be 16-byte aligned.  scale is any finite fp32.
+ * Wp must hold bytes produced by tri_pack2 / tri_pack16 for this K (2-bit code
+ * 3 and 1.6-bit bytes above 242 give unspecified, finite results).  X is
+ * expected finite (a non-finite x may give NaN in every output it touches).
+ * Errors: TRI_EINVAL (a size < 1, K or N >= 2^31, null, unknown fmt),
+ * TRI_EALIGN, TRI_EHIP. */
+int tri_linear(const _Float16 *X, const uint8_t *Wp, float scale,
+               int64_t M, int64_t N, int64_t K, int fmt, _Float16 *Y, hipStream_t stream);
+
+/* tri_linear with the kernel family chosen by the caller (for measurement and
+ * tests).  TRI_ALGO_GEMV needs M == 1 and TRI_FMT_2BIT; TRI_ALGO_SMALLM needs
+ * M <= 16; otherwise TRI_EINVAL.  Results of every family satisfy the same
+ * error bound; they are not bitwise equal to one another. */
+int tri_linear_algo(const _Float16 *X, const uint8_t *Wp, float scale,
+                    int64_t M, int64_t N, int64_t K, int fmt, _Float16 *Y,
+                    int algo, hipStream_t stream);
+
+/* The algorithm tri_linear would pick for (M, N, K, fmt); TRI_EINVAL if invalid. */
+int tri_select_algo(int64_t M, int64_t N, int64_t K, int fmt);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *tri_status_string(int code);
+
+/* ---- Measurement aids (not part of the layer) ----------------------------
+ * tri_probe_read streams `bytes` bytes (a multiple of 16, 16-byte aligned) with
+ * 16-byte loads and writes one word to `sink` (4 bytes) only if a
+ * data-dependent test that practically never holds passes; it is the
+ * size-matched read floor for the weight stream.  tri_probe_copy copies
+ * `bytes` bytes (a multiple of 16, both 16-byte aligned) from src to dst; it
+ * calibrates hardware byte counters.  Errors: TRI_EINVAL, TRI_EALIGN, TRI_EHIP. */
+int tri_probe_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t stream);
+int tri_probe_copy(const void *src, void *dst, int64_t bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TRI_H */

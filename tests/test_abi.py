@@ -1,0 +1,107 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared entry
+point, and rejects bad arguments before launching anything (no GPU needed)."""
+import os
+import re
+import subprocess
+
+import pytest
+
+import bit_mixed_precision_tri_amd as tri
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tri.h")
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tri_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared()
+    assert {"tri_row_bytes", "tri_pack2", "tri_pack16", "tri_unpack", "tri_linear"} <= set(names)
+    out = subprocess.check_output(["nm", "-D", "--defined-only", tri.LIB_PATH], text=True)
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    L = tri.lib()
+    for n in names:
+        assert getattr(L, n) is not None
+
+
+def test_row_bytes():
+    assert tri.tri_row_bytes(4096, tri.TRI_FMT_2BIT) == 1024
+    assert tri.tri_row_bytes(11008, tri.TRI_FMT_2BIT) == 2752
+    assert tri.tri_row_bytes(4096, tri.TRI_FMT_1P6BIT) == 832
+    assert tri.tri_row_bytes(11008, tri.TRI_FMT_1P6BIT) == 2208
+    assert tri.tri_row_bytes(1, tri.TRI_FMT_2BIT) == 16 and tri.tri_row_bytes(81, tri.TRI_FMT_1P6BIT) == 32
+    assert tri.tri_row_bytes(0, tri.TRI_FMT_2BIT) == -1
+    assert tri.tri_row_bytes(10, 5) == -1
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, 7):
+        assert isinstance(tri.tri_status_string(code), str) and tri.tri_status_string(code)
+
+
+def test_select_algo():
+    F2, F16 = tri.TRI_FMT_2BIT, tri.TRI_FMT_1P6BIT
+    assert tri.tri_select_algo(1, 4096, 4096, F2) == tri.TRI_ALGO_GEMV
+    assert tri.tri_select_algo(1, 4096, 4096, F16) == tri.TRI_ALGO_SMALLM
+    assert tri.tri_select_algo(16, 4096, 4096, F2) == tri.TRI_ALGO_SMALLM
+    assert tri.tri_select_algo(17, 4096, 4096, F2) == tri.TRI_ALGO_GEMM
+    assert tri.tri_select_algo(0, 4096, 4096, F2) == tri.TRI_EINVAL
+    assert tri.tri_select_algo(1, 4096, 4096, 3) == tri.TRI_EINVAL
+
+
+# fake device addresses: these calls must fail validation, so nothing is dereferenced or launched
+A, B, C, ODD = 4096, 8192, 12288, 4097
+
+
+def raw(name, *args):
+    return getattr(tri.lib(), name)(*args)
+
+
+def test_linear_argument_errors_launch_nothing():
+    F2 = tri.TRI_FMT_2BIT
+    s = None
+    assert raw("tri_linear", None, B, 1.0, 1, 4, 64, F2, C, s) == tri.TRI_EINVAL
+    assert raw("tri_linear", A, None, 1.0, 1, 4, 64, F2, C, s) == tri.TRI_EINVAL
+    assert raw("tri_linear", A, B, 1.0, 1, 4, 64, F2, None, s) == tri.TRI_EINVAL
+    for (M, N, K) in [(0, 4, 64), (1, 0, 64), (1, 4, 0), (-1, 4, 64), (1, 1 << 31, 64), (1, 4, 1 << 31)]:
+        assert raw("tri_linear", A, B, 1.0, M, N, K, F2, C, s) == tri.TRI_EINVAL
+    assert raw("tri_linear", A, B, 1.0, 1, 4, 64, 2, C, s) == tri.TRI_EINVAL
+    assert raw("tri_linear", ODD, B, 1.0, 1, 4, 64, F2, C, s) == tri.TRI_EALIGN
+    assert raw("tri_linear", A, ODD, 1.0, 1, 4, 64, F2, C, s) == tri.TRI_EALIGN
+    assert raw("tri_linear", A, B, 1.0, 1, 4, 64, F2, ODD, s) == tri.TRI_EALIGN
+    # a kernel family that cannot serve the shape
+    assert raw("tri_linear_algo", A, B, 1.0, 2, 4, 64, F2, C, tri.TRI_ALGO_GEMV, s) == tri.TRI_EINVAL
+    assert raw("tri_linear_algo", A, B, 1.0, 1, 4, 64, tri.TRI_FMT_1P6BIT, C, tri.TRI_ALGO_GEMV, s) == tri.TRI_EINVAL
+    assert raw("tri_linear_algo", A, B, 1.0, 17, 4, 64, F2, C, tri.TRI_ALGO_SMALLM, s) == tri.TRI_EINVAL
+    assert raw("tri_linear_algo", A, B, 1.0, 1, 4, 64, F2, C, 9, s) == tri.TRI_EINVAL
+
+
+def test_pack_argument_errors_launch_nothing():
+    s = None
+    for name in ("tri_pack2", "tri_pack16"):
+        assert raw(name, None, 4, 64, B, s) == tri.TRI_EINVAL
+        assert raw(name, A, 4, 64, None, s) == tri.TRI_EINVAL
+        assert raw(name, A, 0, 64, B, s) == tri.TRI_EINVAL
+        assert raw(name, A, 4, 0, B, s) == tri.TRI_EINVAL
+        assert raw(name, A, 4, 64, ODD, s) == tri.TRI_EALIGN
+    assert raw("tri_unpack", B, 4, 64, 2, A, s) == tri.TRI_EINVAL
+    assert raw("tri_unpack", ODD, 4, 64, 0, A, s) == tri.TRI_EALIGN
+    assert raw("tri_unpack", B, 4, 64, 0, None, s) == tri.TRI_EINVAL
+
+
+def test_probe_argument_errors_launch_nothing():
+    assert raw("tri_probe_read", A, 15, B, None) == tri.TRI_EINVAL
+    assert raw("tri_probe_read", ODD, 16, B, None) == tri.TRI_EALIGN
+    assert raw("tri_probe_copy", A, B, 24, None) == tri.TRI_EINVAL
+    assert raw("tri_probe_copy", A, ODD, 32, None) == tri.TRI_EALIGN
+
+
+def test_binding_raises_on_error_status():
+    with pytest.raises(tri.TriError):
+        tri.tri_linear(A, B, 1.0, 0, 4, 64, tri.TRI_FMT_2BIT, C, stream=0)

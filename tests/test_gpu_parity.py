@@ -1,0 +1,281 @@
+"""GPU parity: libtri (HIP, gfx950) against the CPU oracle, element by element.
+
+Packing and unpacking must be bit-exact; the layer must satisfy, for every
+element, |Y - Y_ref| <= 2e-3*|scale|*sum_k|x_k| + 1e-3*|Y_ref| with Y_ref the
+unrounded float64 oracle value.  Every input is seeded (PCG64, [workload, layer,
+stream]); the shapes are those of the synthetic workloads plus ragged ones.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import bit_mixed_precision_tri_amd as tri
+from bit_mixed_precision_tri_amd import configs, synth
+from tests.gpu_helpers import say, cuda, host, algos_for, check_layer
+from tests import block_glue
+
+pytestmark = pytest.mark.gpu
+
+F2, F16 = tri.TRI_FMT_2BIT, tri.TRI_FMT_1P6BIT
+FMTS = [F2, F16]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    tri.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- packing
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_pack_bit_exact_ragged(fmt):
+    rng = synth.rng_for(100, fmt, 0)
+    for N in (1, 3, 37):
+        for K in (1, 2, 3, 4, 5, 6, 63, 64, 65, 79, 80, 81, 159, 160, 161, 512, 1000, 4095, 4097, 11008):
+            W = synth.trits(rng, N, K)
+            W[0, :: 7] = rng.integers(-128, 128, W[0, :: 7].shape)     # any int8: the sign is encoded
+            got = host(tri.pack(cuda(W), fmt))
+            np.testing.assert_array_equal(got, oracle.pack(W, fmt), err_msg="N=%d K=%d" % (N, K))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_unpack_every_byte_value_bit_exact(fmt):
+    K = 4 if fmt == F2 else 5
+    S = tri.tri_row_bytes(K, fmt)
+    Wp = np.zeros((256, S), np.uint8)
+    Wp[:, 0] = np.arange(256)
+    Wp[:, 1:] = np.arange(256)[::-1, None]       # every byte value in the padding too
+    got = host(tri.unpack(cuda(Wp), K, fmt))
+    np.testing.assert_array_equal(got, oracle.unpack(Wp, K, fmt))
+    Kfull = S * (4 if fmt == F2 else 5)          # decode the whole row, all 256 values per position
+    np.testing.assert_array_equal(host(tri.unpack(cuda(Wp), Kfull, fmt)), oracle.unpack(Wp, Kfull, fmt))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_unpack_roundtrip(fmt):
+    rng = synth.rng_for(101, fmt, 0)
+    for (N, K) in [(5, 1), (7, 333), (64, 4096), (3, 11008)]:
+        W = synth.trits(rng, N, K)
+        Wp = tri.pack(cuda(W), fmt)
+        np.testing.assert_array_equal(host(tri.unpack(Wp, K, fmt)), W)
+
+
+# ---------------------------------------------------------------- the layer, small and ragged shapes
+
+def run_layer(X, Wp_dev, scale, K, fmt, algo):
+    return host(tri.linear(cuda(X), Wp_dev, scale, K, fmt, algo=algo))
+
+
+def test_small_layer_both_formats_all_algos():
+    cfg = configs.SMALL
+    for fmt in cfg["fmts"]:
+        W, X, s = synth.layer_inputs(cfg["workload_id"], 0, cfg["M"], cfg["N"], cfg["K"], cfg["scale"])
+        Wp = tri.pack(cuda(W), fmt)
+        for algo in algos_for(cfg["M"], fmt) + [tri.TRI_ALGO_AUTO]:
+            say("small layer fmt=%d algo=%d" % (fmt, algo))
+            Y = run_layer(X, Wp, s, cfg["K"], fmt, algo)
+            worst, exact = check_layer(Y, X, W, s, "small fmt=%d algo=%d" % (fmt, algo))
+            say("  worst err/tol %.3g, fraction equal to fp16(ref) %.3f" % (worst, exact))
+
+
+RAGGED = [(1, 1, 1), (1, 37, 1000), (1, 130, 4097), (1, 300, 81), (1, 33, 12000), (2, 17, 65), (3, 129, 333),
+          (5, 300, 81), (16, 50, 4097), (16, 1, 160), (7, 1025, 640), (17, 40, 200), (40, 70, 700),
+          (64, 96, 513), (130, 257, 1111)]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("shape", RAGGED, ids=["M%dN%dK%d" % s for s in RAGGED])
+def test_layer_ragged_shapes(fmt, shape):
+    M, N, K = shape
+    W, X, s = synth.layer_inputs(200 + fmt, M * 7 + N, M, N, K)
+    Wp = tri.pack(cuda(W), fmt)
+    for algo in algos_for(M, fmt):
+        say("ragged M=%d N=%d K=%d fmt=%d algo=%d" % (M, N, K, fmt, algo))
+        check_layer(run_layer(X, Wp, s, K, fmt, algo), X, W, s, "M=%d N=%d K=%d fmt=%d algo=%d" % (M, N, K, fmt, algo))
+
+
+def test_special_values():
+    """Zero weights, all +1 weights, a one-hot activation, a negative scale, fp16 extremes.
+    (The scales keep every |Y| below the fp16 range; overflow is covered by test_overflow_to_inf.)"""
+    M, N, K = 3, 40, 700
+    rng = synth.rng_for(210, 0, 0)
+    X = synth.activations(rng, M, K)
+    X[1, :5] = [65504, -65504, 6.1e-5, 6e-8, -6e-8]     # largest, smallest normal, subnormals
+    X[2] = 0
+    X[2, 123] = 1
+    for fmt in FMTS:
+        for W in (np.zeros((N, K), np.int8), np.ones((N, K), np.int8), synth.trits(rng, N, K)):
+            Wp = tri.pack(cuda(W), fmt)
+            for algo in algos_for(M, fmt):
+                for s in (0.02, -0.375):
+                    Y = run_layer(X, Wp, s, K, fmt, algo)
+                    check_layer(Y, X, W, s, "special fmt=%d algo=%d" % (fmt, algo))
+                    if not W.any():
+                        assert np.all(Y == 0)
+                    # a one-hot activation row returns fp16(scale * t[:, 123]) exactly
+                    np.testing.assert_array_equal(Y[2], (np.float32(s) * W[:, 123]).astype(np.float16))
+
+
+def test_overflow_to_inf():
+    """Results beyond the fp16 range round to +-inf (round to nearest even), as the oracle's fp16 rounding does."""
+    M, N, K = 2, 64, 256
+    X = np.full((M, K), 60000, np.float16)
+    X[1] = -1.0
+    W = np.ones((N, K), np.int8)
+    W[1::2] = -1
+    for fmt in FMTS:
+        Wp = tri.pack(cuda(W), fmt)
+        for algo in algos_for(M, fmt):
+            Y = run_layer(X, Wp, 1.0, K, fmt, algo)
+            with np.errstate(over="ignore"):
+                Yref = oracle.linear_f64(X, W, 1.0).astype(np.float16)
+            np.testing.assert_array_equal(Y, Yref)          # +-inf in row 0, exact small values in row 1
+            assert np.isinf(Y[0]).all()
+
+
+# ---------------------------------------------------------------- invariants
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_invariants(fmt):
+    """Deterministic; 2*scale gives 2*Y bitwise (outside the fp16 subnormal range); -X, -W and a
+    consistent k permutation stay within tolerance.  (-X does not give -Y bitwise: neither
+    v_dot2_f32_f16 nor the MFMA accumulation rounds sign-symmetrically; the fraction is printed.)"""
+    import torch
+    for (M, N, K) in [(1, 300, 4096), (8, 200, 1000), (40, 130, 700)]:
+        W, X, s = synth.layer_inputs(220 + fmt, M, M, N, K)
+        Wp = tri.pack(cuda(W), fmt)
+        Wn = tri.pack(cuda(-W), fmt)
+        Xd = cuda(X)
+        for algo in algos_for(M, fmt):
+            what = "M=%d N=%d K=%d fmt=%d algo=%d" % (M, N, K, fmt, algo)
+            Y1 = host(tri.linear(Xd, Wp, s, K, fmt, algo=algo))
+            Y2 = host(tri.linear(Xd, Wp, s, K, fmt, algo=algo))
+            np.testing.assert_array_equal(Y1.view(np.uint16), Y2.view(np.uint16), err_msg=what)
+            Y2s = host(tri.linear(Xd, Wp, 2 * s, K, fmt, algo=algo))
+            normal = np.abs(Y1) >= np.float16(2.0 ** -13)
+            np.testing.assert_array_equal(Y2s[normal], 2 * Y1[normal], err_msg=what)
+            Yneg = host(tri.linear(-Xd, Wp, s, K, fmt, algo=algo))
+            check_layer(Yneg, -X, W, s, "negated X " + what)
+            say("%s: -X gives -Y bitwise for %.3f of outputs" % (what, float(np.mean(Yneg == -Y1))))
+            check_layer(host(tri.linear(Xd, Wn, s, K, fmt, algo=algo)), X, -W, s, "negated W " + what)
+            perm = np.random.default_rng(5).permutation(K)
+            Yp = host(tri.linear(cuda(X[:, perm]), tri.pack(cuda(W[:, perm]), fmt), s, K, fmt, algo=algo))
+            check_layer(Yp, X, W, s, "k-permuted " + what)
+        del Xd
+        torch.cuda.synchronize()
+
+
+def test_misaligned_device_pointer_rejected():
+    import torch
+    X = torch.zeros(1, 65, dtype=torch.float16, device="cuda")
+    Wp = torch.zeros(4, 32, dtype=torch.uint8, device="cuda")
+    Y = torch.zeros(1, 4, dtype=torch.float16, device="cuda")
+    with pytest.raises(tri.TriError) as e:
+        tri.tri_linear(X[:, 1:], Wp, 1.0, 1, 4, 64, F2, Y)
+    assert e.value.code == tri.TRI_EALIGN
+
+
+def test_probe_kernels():
+    import torch
+    src = torch.arange(1 << 20, dtype=torch.int32, device="cuda")
+    dst = torch.zeros_like(src)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    tri.tri_probe_copy(src, dst, src.numel() * 4)
+    tri.tri_probe_read(src, src.numel() * 4, sink)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
+
+
+# ---------------------------------------------------------------- the synthetic workloads at full size
+
+@pytest.mark.parametrize("shape", configs.DECODE_SHAPES, ids=[s[0] for s in configs.DECODE_SHAPES])
+def test_decode_gemv_full_size(shape):
+    name, K, N = shape
+    cfg = configs.DECODE
+    W, X, s = synth.layer_inputs(cfg["workload_id"], configs.DECODE_SHAPES.index(shape), 1, N, K)
+    Wp = tri.pack(cuda(W), F2)
+    np.testing.assert_array_equal(host(Wp), oracle.pack2(W))
+    for algo in [tri.TRI_ALGO_AUTO] + algos_for(1, F2):
+        say("decode %s algo=%d" % (name, algo))
+        worst, exact = check_layer(run_layer(X, Wp, s, K, F2, algo), X, W, s, "decode %s algo %d" % (name, algo))
+        say("  worst err/tol %.3g, fraction equal to fp16(ref) %.3f" % (worst, exact))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_batched_decode_full_size(fmt):
+    cfg = configs.BATCHED
+    for li, (name, K, N) in enumerate(cfg["shapes"]):
+        W = synth.trits(synth.rng_for(cfg["workload_id"], li, synth.STREAM_W), N, K)
+        Wp = tri.pack(cuda(W), fmt)
+        Wp_h = host(Wp)
+        np.testing.assert_array_equal(Wp_h, oracle.pack(W, fmt))
+        np.testing.assert_array_equal(host(tri.unpack(Wp, K, fmt)), oracle.unpack(Wp_h, K, fmt))
+        for M in cfg["Ms"]:
+            X = synth.activations(synth.rng_for(cfg["workload_id"], 10 * li + M, synth.STREAM_X), M, K)
+            s = synth.uniform_scale(synth.rng_for(cfg["workload_id"], li, synth.STREAM_SCALE))
+            say("batched %s M=%d fmt=%d" % (name, M, fmt))
+            worst, exact = check_layer(run_layer(X, Wp, s, K, fmt, tri.TRI_ALGO_AUTO), X, W, s,
+                                       "batched %s M=%d fmt=%d" % (name, M, fmt))
+            say("  worst err/tol %.3g, fraction equal to fp16(ref) %.3f" % (worst, exact))
+
+
+@pytest.mark.parametrize("M", configs.BLOCK["Ms"])
+def test_block_step(M):
+    """Seven chained linears of one decode block; every linear is checked on its actual input."""
+    cfg = configs.BLOCK
+    layers = {}
+    for li, (name, K, N) in enumerate(cfg["layers"]):
+        W = synth.trits(synth.rng_for(cfg["workload_id"], li, synth.STREAM_W), N, K)
+        s = synth.uniform_scale(synth.rng_for(cfg["workload_id"], li, synth.STREAM_SCALE))
+        layers[name] = (W, tri.pack(cuda(W), cfg["fmt"]), s, K)
+    x0 = synth.activations(synth.rng_for(cfg["workload_id"], 100 + M, synth.STREAM_X), M, cfg["hidden"])
+
+    def gpu_linear(name, a):
+        W, Wp, s, K = layers[name]
+        Y = run_layer(a, Wp, s, K, cfg["fmt"], tri.TRI_ALGO_AUTO)
+        check_layer(Y, a, W, s, "block M=%d layer %s" % (M, name))
+        return Y
+
+    def ref_linear(name, a):
+        W, _, s, _ = layers[name]
+        return oracle.linear_f64(a, W, s).astype(np.float16)
+
+    say("block step M=%d" % M)
+    out_gpu, _ = block_glue.block_step(x0, gpu_linear)
+    out_ref, _ = block_glue.block_step(x0, ref_linear)
+    rel = np.linalg.norm(out_gpu - out_ref) / np.linalg.norm(out_ref)
+    say("  block output relative difference GPU chain vs oracle chain: %.3g" % rel)
+    assert rel < 1e-2
+
+
+PREFILL_ROWS = [0, 1, 2, 15, 16, 127, 128, 255, 256, 1023, 1024, 1500, 2046, 2047]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("li", [0, 1])
+def test_prefill_full_size_sampled_rows(fmt, li):
+    import torch
+    cfg = configs.PREFILL
+    name, K, N = cfg["shapes"][li]
+    M = cfg["M"]
+    say("prefill %s fmt=%d: generating inputs" % (name, fmt))
+    W = synth.trits(synth.rng_for(cfg["workload_id"], li, synth.STREAM_W), N, K)
+    X = synth.activations(synth.rng_for(cfg["workload_id"], li, synth.STREAM_X), M, K)
+    s = cfg["scale"]
+    Wd = cuda(W)
+    Wp = tri.pack(Wd, fmt)
+    del Wd
+    say("prefill %s fmt=%d: pack check" % (name, fmt))
+    np.testing.assert_array_equal(host(Wp), oracle.pack(W, fmt))
+    say("prefill %s fmt=%d: linear" % (name, fmt))
+    Y = run_layer(X, Wp, s, K, fmt, tri.TRI_ALGO_AUTO)
+    assert np.all(np.isfinite(Y))
+    worst, exact = check_layer(Y, X, W, s, "prefill %s fmt=%d" % (name, fmt), rows=PREFILL_ROWS)
+    say("  worst err/tol %.3g, fraction equal to fp16(ref) %.3f" % (worst, exact))
+    del Wp
+    torch.cuda.empty_cache()
