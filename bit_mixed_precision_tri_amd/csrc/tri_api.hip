@@ -43,7 +43,9 @@ int run_linear(const _Float16 *X, const uint8_t *Wp, float scale, int64_t M, int
         return launch_gemv2(x, Wp, scale, (int)N, (int)K, y, s);
     case TRI_ALGO_SMALLM:
         if (M > 16) return TRI_EINVAL;
-        return launch_smallm(x, Wp, scale, (int)M, (int)N, (int)K, fmt, y, s);
+        if (launch_decode(x, Wp, scale, (int)M, (int)N, (int)K, fmt, y, s))
+            return hipGetLastError() == hipSuccess ? TRI_OK : TRI_EHIP;
+        return launch_smallm(x, Wp, scale, (int)M, (int)N, (int)K, fmt, y, s);   // long rows: streaming variant
     case TRI_ALGO_GEMM:
         return launch_gemm(x, Wp, scale, M, (int)N, (int)K, fmt, y, s);
     default:

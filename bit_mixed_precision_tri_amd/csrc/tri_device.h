@@ -35,6 +35,39 @@ __device__ __forceinline__ uint32_t pair_halves(uint32_t hi, uint32_t lo)
     return perm(hi, lo, E == 0 ? 0x05040100u : 0x07060302u);
 }
 
+// v_mfma_f32_16x16x32_f16: D[16x16] += A[16x32] * B[32x16]; lane (g = lane/16, l = lane%16)
+// supplies A[l][8g..8g+7] and B[8g..8g+7][l] as four registers of fp16 pairs and holds
+// D[4g..4g+3][l] (layout and fp16-subnormal handling verified on gfx950).
+__device__ __forceinline__ float4_t mfma16(const uint32_t a0, const uint32_t a1, const uint32_t a2, const uint32_t a3,
+                                           const uint32_t b0, const uint32_t b1, const uint32_t b2, const uint32_t b3,
+                                           float4_t c)
+{
+    const u32x4 av = {a0, a1, a2, a3};
+    const u32x4 bv = {b0, b1, b2, b3};
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), __builtin_bit_cast(half8_t, bv), c,
+                                                  0, 0, 0);
+}
+
+__device__ __forceinline__ float4_t mfma16(const uint4 a, const uint32_t b0, const uint32_t b1, const uint32_t b2,
+                                           const uint32_t b3, float4_t c)
+{
+    return mfma16(a.x, a.y, a.z, a.w, b0, b1, b2, b3, c);
+}
+
+// The five base-3 digits of byte b (digit j = floor(b / 3^j) mod 3), two bits each at bits 2j:
+// the table that turns a 1.6-bit byte into the 2-bit digit layout.
+__device__ __forceinline__ uint32_t base3_digits_2bit(uint32_t b)
+{
+    uint32_t code = 0;
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+        const uint32_t q = b / 3u;
+        code |= (b - 3u * q) << (2 * j);
+        b = q;
+    }
+    return code;
+}
+
 // 16-byte global load.
 __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
 

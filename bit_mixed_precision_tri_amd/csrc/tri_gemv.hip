@@ -173,10 +173,8 @@ template <int PM>
 static void launch_pm(const uint16_t *X, const uint8_t *Wp, float scale, int N, int K, int C, uint16_t *Y,
                       hipStream_t s)
 {
-    // rows per wave: as many as still keep >= ~1024 waves (one per SIMD) in flight
-    if (N >= 1024 * 8) launch_cfg<8, PM>(X, Wp, scale, N, K, C, Y, s);
-    else if (N >= 1024 * 4) launch_cfg<4, PM>(X, Wp, scale, N, K, C, Y, s);
-    else if (N >= 1024 * 2) launch_cfg<2, PM>(X, Wp, scale, N, K, C, Y, s);
+    // rows per wave: measured best is 1 while that still gives >= ~4 waves per SIMD, else 2
+    if (N > 4096 || PM > 1) launch_cfg<2, PM>(X, Wp, scale, N, K, C, Y, s);
     else launch_cfg<1, PM>(X, Wp, scale, N, K, C, Y, s);
 }
 

@@ -21,6 +21,9 @@ int launch_unpack(const uint8_t *Wp, int64_t N, int64_t K, int fmt, int8_t *W, h
 int launch_gemv2(const uint16_t *X, const uint8_t *Wp, float scale, int N, int K, uint16_t *Y, hipStream_t s);
 int launch_smallm(const uint16_t *X, const uint8_t *Wp, float scale, int M, int N, int K, int fmt, uint16_t *Y,
                   hipStream_t s);
+// MFMA decode kernel with activations staged in LDS; false (nothing launched) if K is too long for it.
+bool launch_decode(const uint16_t *X, const uint8_t *Wp, float scale, int M, int N, int K, int fmt, uint16_t *Y,
+                   hipStream_t s);
 int launch_gemm(const uint16_t *X, const uint8_t *Wp, float scale, int64_t M, int N, int K, int fmt, uint16_t *Y,
                 hipStream_t s);
 int launch_probe_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t s);

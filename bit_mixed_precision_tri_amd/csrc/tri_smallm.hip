@@ -38,29 +38,6 @@
 
 namespace tri {
 
-__device__ __forceinline__ float4_t mfma16(const uint32_t a0, const uint32_t a1, const uint32_t a2, const uint32_t a3,
-                                           const uint32_t b0, const uint32_t b1, const uint32_t b2, const uint32_t b3,
-                                           float4_t c)
-{
-    const u32x4 av = {a0, a1, a2, a3};
-    const u32x4 bv = {b0, b1, b2, b3};
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), __builtin_bit_cast(half8_t, bv), c,
-                                                  0, 0, 0);
-}
-
-// Five base-3 digits of byte b at bits 2j (digit j = floor(b / 3^j) mod 3).
-__device__ __forceinline__ uint32_t base3_digits_2bit(uint32_t b)
-{
-    uint32_t code = 0;
-#pragma unroll
-    for (int j = 0; j < 5; ++j) {
-        const uint32_t q = b / 3u;
-        code |= (b - 3u * q) << (2 * j);
-        b = q;
-    }
-    return code;
-}
-
 template <int FMT, int R, int NW>
 __global__ __launch_bounds__(64 * NW) void k_smallm(const uint16_t *__restrict__ X, const uint8_t *__restrict__ Wp,
                                                     float scale, int M, int N, int K, int C,
@@ -243,23 +220,18 @@ template <int FMT>
 static void launch_fmt(const uint16_t *X, const uint8_t *Wp, float scale, int M, int N, int K, int C, uint16_t *Y,
                        hipStream_t s)
 {
-    // K split across waves: enough lane-group slots (4 per wave) to keep >= ~2048 waves busy
-    const int nw = C >= 64 ? 8 : (C >= 32 ? 4 : (C >= 16 ? 2 : 1));
-    const bool two_blocks = (int64_t)((N + 31) / 32) * nw >= 2048;
-    if (two_blocks) {
-        switch (nw) {
-        case 8: launch_cfg<FMT, 2, 8>(X, Wp, scale, M, N, K, C, Y, s); break;
-        case 4: launch_cfg<FMT, 2, 4>(X, Wp, scale, M, N, K, C, Y, s); break;
-        case 2: launch_cfg<FMT, 2, 2>(X, Wp, scale, M, N, K, C, Y, s); break;
-        default: launch_cfg<FMT, 2, 1>(X, Wp, scale, M, N, K, C, Y, s); break;
-        }
+    // K split across up to 8 waves; two 16-row blocks per wave once M is large enough to
+    // make the activation re-reads the larger cost
+    if (C >= 64) {
+        if (M > 8 && K <= 4096) launch_cfg<FMT, 2, 8>(X, Wp, scale, M, N, K, C, Y, s);
+        else if (K <= 4096) launch_cfg<FMT, 1, 4>(X, Wp, scale, M, N, K, C, Y, s);
+        else launch_cfg<FMT, 1, 8>(X, Wp, scale, M, N, K, C, Y, s);
+    } else if (C >= 32) {
+        launch_cfg<FMT, 1, 4>(X, Wp, scale, M, N, K, C, Y, s);
+    } else if (C >= 16) {
+        launch_cfg<FMT, 1, 2>(X, Wp, scale, M, N, K, C, Y, s);
     } else {
-        switch (nw) {
-        case 8: launch_cfg<FMT, 1, 8>(X, Wp, scale, M, N, K, C, Y, s); break;
-        case 4: launch_cfg<FMT, 1, 4>(X, Wp, scale, M, N, K, C, Y, s); break;
-        case 2: launch_cfg<FMT, 1, 2>(X, Wp, scale, M, N, K, C, Y, s); break;
-        default: launch_cfg<FMT, 1, 1>(X, Wp, scale, M, N, K, C, Y, s); break;
-        }
+        launch_cfg<FMT, 1, 1>(X, Wp, scale, M, N, K, C, Y, s);
     }
 }
 
