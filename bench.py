@@ -4,21 +4,28 @@
 Headline workload: decode GEMV at M = 1 with 2-bit packed ternary weights, the
 three projections of a LLaMA-style block at hidden 4096 / MLP 11008
 (4096x4096, 4096->11008, 11008->4096).  One step = the three tri_linear launches
-on fresh (cold) weights: each step reads a different copy of every packed
-matrix from a pool of >= 1 GiB, so the 256 MB Infinity Cache cannot serve them.
-The value is effective HBM bandwidth: (packed weights as stored + fp16 X read +
-fp16 Y written) per step / wall time per step, inputs resident in HBM.
+on cold weights: every matrix rotates over 64 distinct copies (1.7 GB in all),
+so the 256 MB Infinity Cache cannot serve a step's weights.  The value is
+effective HBM bandwidth: (packed weights as stored + fp16 X read + fp16 Y
+written) per step / wall time per step, inputs resident in HBM.
 
-The same JSON line also carries the roofline fraction of the GEMV kernel
-(HIP-event-timed launch durations), the size-matched streaming-read floor, the
-CPU oracle timed on this host, and the batched-decode and prefill workloads.
+Timing.  The timed region replays a HIP graph of the steps (captured once from
+the same tri_linear calls), so the host's per-launch cost stays out of it.
+Per-kernel durations come from HIP events on the launch stream around a batch
+of back-to-back launches of one kernel, queued while a sleep kernel holds the
+GPU, so no host time enters them (they agree with rocprofv3's per-dispatch
+durations).
 
-  python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--skip-extra] [--skip-cpu]
+The same JSON line carries the roofline fraction of the GEMV kernel, the
+size-matched streaming-read floor, the CPU oracle timed on this host, and the
+batched-decode, block-step and prefill workloads.
+
+  python bench.py [--gpus 1] [--steps 1000] [--warmup 20] [--skip-extra] [--skip-cpu]
 """
 import argparse
-import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -29,7 +36,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E peak, GB/s
 MFMA_F16_PEAK_TFLOPS = 2516.6   # MI355X dense fp16 MFMA peak (256 CU x 4096 flop/clk x 2.4 GHz)
 METRIC = "effective HBM GB/s (% of peak) for M=1 ternary GEMV; prefill GEMM TFLOP/s (% MFMA)"
-POOL_BYTES = 1 << 30            # rotate every weight matrix over >= 1 GiB of copies
+COPIES = 64                     # distinct copies of every decode weight matrix
+COUNTERS = os.path.join(ROOT, "profiles", "decode_gemv_counters.md")
 
 
 def log(*a):
@@ -42,20 +50,18 @@ def effective_bytes(M, N, K, fmt):
 
 
 class Layer:
-    """One ternary linear on the GPU with a rotating pool of packed-weight copies."""
+    """One ternary linear on the GPU with a pool of distinct packed-weight copies."""
 
-    def __init__(self, workload_id, layer_id, M, N, K, fmt, scale=None, pool_bytes=POOL_BYTES, max_copies=64):
+    def __init__(self, workload_id, layer_id, M, N, K, fmt, scale=None, copies=COPIES, X=None):
         import torch
         import bit_mixed_precision_tri_amd as tri
         from bit_mixed_precision_tri_amd import synth
         self.M, self.N, self.K, self.fmt = M, N, K, fmt
-        W, X, self.scale = synth.layer_inputs(workload_id, layer_id, M, N, K, scale)
+        W, Xh, self.scale = synth.layer_inputs(workload_id, layer_id, M, N, K, scale)
         Wp = tri.pack(torch.from_numpy(W).cuda(), fmt)
-        self.S = Wp.shape[1]
-        ncopies = max(1, min(max_copies, -(-pool_bytes // Wp.numel())))
-        self.pool = torch.empty((ncopies,) + tuple(Wp.shape), dtype=torch.uint8, device="cuda")
+        self.pool = torch.empty((copies,) + tuple(Wp.shape), dtype=torch.uint8, device="cuda")
         self.pool[:] = Wp                       # distinct addresses, same content
-        self.X = torch.from_numpy(X).cuda()
+        self.X = X if X is not None else torch.from_numpy(Xh).cuda()
         self.Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
         self.bytes = effective_bytes(M, N, K, fmt)
         self.flops = 2 * M * N * K
@@ -71,54 +77,78 @@ class Layer:
             tri.tri_linear(self.X, Wp, self.scale, self.M, self.N, self.K, self.fmt, self.Y)
 
 
-def time_launches(layer, reps, warmup, algo=0):
-    """Average kernel duration (s) from HIP events around each launch, cold weights."""
-    import torch
-    for _ in range(warmup):
-        layer.launch(algo)
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for a, b in evs:
+class Clock:
+    """Back-to-back kernel timing with HIP events on the current (launch) stream."""
+
+    def __init__(self):
+        import torch
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1000)                  # first call compiles/loads the sleep kernel
         a.record()
-        layer.launch(algo)
+        torch.cuda._sleep(5_000_000)
         b.record()
-    torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in evs) / reps / 1e3
+        torch.cuda.synchronize()
+        self.cycles_per_us = 5_000_000 / (a.elapsed_time(b) * 1e3)
+
+    def hold(self, us):
+        """Queue a sleep kernel that keeps the GPU busy for about `us` microseconds."""
+        import torch
+        torch.cuda._sleep(int(us * self.cycles_per_us))
+
+    def run(self, calls, warmup=5):
+        """Run the callables back to back on the GPU; mean time per call (s).
+
+        A sleep kernel holds the GPU until every call is queued, and one pair of events
+        brackets the batch, so the figure is kernel duration plus the launch gap of an
+        in-order stream, with no host time in it.  Also returns whether the queue stayed
+        ahead of the GPU."""
+        import torch
+        for c in calls[:warmup]:
+            c()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        hold_us = 40.0 * len(calls) + 5000.0      # generous host cost per queued call
+        self.hold(hold_us)
+        t0 = time.perf_counter()
+        a.record()
+        for c in calls:
+            c()
+        b.record()
+        host_us = (time.perf_counter() - t0) * 1e6
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / 1e3 / len(calls), host_us < 0.8 * hold_us
 
 
-def read_floor(nbytes, reps=200):
-    """Size-matched streaming read (tri_probe_read) over a rotating >= 1 GiB pool: average duration (s)."""
+def read_floor(nbytes, clock, reps=200):
+    """Size-matched streaming read (tri_probe_read) over a rotating >= 1 GiB pool: mean duration (s)."""
     import torch
     import bit_mixed_precision_tri_amd as tri
     nb = (nbytes + 15) // 16 * 16
-    ncopies = max(1, -(-POOL_BYTES // nb))
+    ncopies = max(1, -(-(1 << 30) // nb))
     pool = torch.empty((ncopies, nb), dtype=torch.uint8, device="cuda")
     pool.fill_(1)
     sink = torch.zeros(4, dtype=torch.int32, device="cuda")
-    for i in range(20):
-        tri.tri_probe_read(pool[i % ncopies], nb, sink)
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for i, (a, b) in enumerate(evs):
-        a.record()
-        tri.tri_probe_read(pool[i % ncopies], nb, sink)
-        b.record()
-    torch.cuda.synchronize()
-    t = sum(a.elapsed_time(b) for a, b in evs) / reps / 1e3
+    calls = [(lambda i=i: tri.tri_probe_read(pool[i % ncopies], nb, sink)) for i in range(reps)]
+    t, _ = clock.run(calls)
     del pool
     torch.cuda.empty_cache()
     return t
 
 
-def counters_for(kernel_file):
-    """HBM traffic per launch from the committed rocprofv3 counter summary, if it matches the current source."""
-    path = os.path.join(ROOT, "profiles", "decode_gemv2_counters.json")
-    if not os.path.exists(path):
+def counters():
+    """HBM traffic of the GEMV kernel per decode step from the committed rocprofv3 summary,
+    or None when the kernel source changed after the counters were taken."""
+    import hashlib
+    if not os.path.exists(COUNTERS):
         return None
-    rec = json.load(open(path))
-    src = open(os.path.join(ROOT, "bit_mixed_precision_tri_amd", "csrc", kernel_file), "rb").read()
+    m = re.search(r"^traffic-json: (\{.*\})\s*$", open(COUNTERS).read(), re.M)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    src = open(os.path.join(ROOT, "bit_mixed_precision_tri_amd", "csrc", rec["source"]), "rb").read()
     if rec.get("source_sha256") != hashlib.sha256(src).hexdigest():
-        return None                     # the kernel changed since the counters were taken
+        return None
     return rec
 
 
@@ -144,24 +174,46 @@ def cpu_baseline(shapes, budget_s=10.0):
             break
     t = float(np.median(times))
     return {"value": round(total_bytes / t / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": "full decode step (3 shapes, M=1, 2-bit: unpack + float64 layer), median of %d runs, "
-                      "%.3f s per step" % (len(times), t)}
+            "sample": "the full decode step (3 shapes, M=1, 2-bit: unpack + float64 layer) run %d times in ~%d s, "
+                      "median %.3f s per step" % (len(times), budget_s, t)}
+
+
+def capture(layers, steps):
+    """A HIP graph of `steps` decode steps (each: every layer once, next weight copy)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for L in layers:
+            L.launch()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for _ in range(steps):
+            for L in layers:
+                L.launch()
+    torch.cuda.synchronize()
+    return g
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--skip-extra", action="store_true", help="skip the batched-decode and prefill workloads")
+    ap.add_argument("--skip-extra", action="store_true", help="skip the batched, block and prefill workloads")
     ap.add_argument("--skip-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--profile", choices=["decode", "batched", "prefill", "copy"],
-                    help="only launch one workload a few times (for rocprofv3 runs)")
+    ap.add_argument("--profile", choices=["decode", "copy"],
+                    help="only launch one workload a few times (for rocprofv3 --pmc runs)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs the ternary linear layer on one GPU only; --gpus %d is not supported"
-              % max(args.gpus, world), file=sys.stderr)
+        print("bench.py: the ternary linear layer runs on one GPU here; --gpus %d is not supported "
+              "(multi-GPU sharding is a design note only)" % max(args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("bench.py: --steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -170,7 +222,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     tri.lib()
     torch.cuda.set_device(0)
-    F2, F16 = tri.TRI_FMT_2BIT, tri.TRI_FMT_1P6BIT
+    F2 = tri.TRI_FMT_2BIT
 
     if args.profile:
         return profile_mode(args.profile)
@@ -179,32 +231,38 @@ def main():
     dcfg = configs.DECODE
     layers = [Layer(dcfg["workload_id"], li, 1, N, K, F2) for li, (name, K, N) in enumerate(dcfg["shapes"])]
     step_bytes = sum(L.bytes for L in layers)
-    for _ in range(args.warmup):
-        for L in layers:
-            L.launch()
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in layers]
-           for _ in range(args.steps)]
+    chunk = min(args.steps, COPIES)
+    g_main = capture(layers, chunk)
+    g_rest = capture(layers, args.steps % chunk) if args.steps % chunk else None
+    for _ in range(max(1, args.warmup // chunk)):
+        g_main.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for step in range(args.steps):
-        for L, (a, b) in zip(layers, evs[step]):
-            a.record()
-            L.launch()
-            b.record()
+    for _ in range(args.steps // chunk):
+        g_main.replay()
+    if g_rest is not None:
+        g_rest.replay()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    per_launch = [sum(evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)) / args.steps / 1e3
-                  for i in range(len(layers))]
     value = step_bytes * args.steps / elapsed / 1e9
+    del g_main, g_rest
+
+    # per-kernel durations: 200 back-to-back launches of each shape (rotating weight copies)
+    clock = Clock()
+    per_launch, ahead = [], True
+    for L in layers:
+        t, ok = clock.run([L.launch] * 200)
+        per_launch.append(t)
+        ahead = ahead and ok
     achieved = step_bytes / sum(per_launch) / 1e9
     shapes_out = []
     for (name, K, N), L, t in zip(dcfg["shapes"], layers, per_launch):
         shapes_out.append({"shape": name, "K": K, "N": N, "bytes": L.bytes, "kernel_us": round(t * 1e6, 3),
                            "GBps": round(L.bytes / t / 1e9, 1),
                            "algo": tri.ALGO_NAMES[tri.tri_select_algo(1, N, K, F2)]})
-    # the smallm MFMA kernel at M = 1, same shapes (kernel choice evidence)
+    # the small-M MFMA kernels at M = 1, same shapes (kernel choice evidence)
     for so, L in zip(shapes_out, layers):
-        t = time_launches(L, 100, 10, algo=tri.TRI_ALGO_SMALLM)
+        t, _ = clock.run([lambda L=L: L.launch(tri.TRI_ALGO_SMALLM)] * 100)
         so["smallm_kernel_us"] = round(t * 1e6, 3)
         so["smallm_GBps"] = round(L.bytes / t / 1e9, 1)
     del layers
@@ -212,43 +270,45 @@ def main():
     floors = []
     for (name, K, N) in dcfg["shapes"]:
         nb = N * tri.tri_row_bytes(K, F2)
-        t = read_floor(nb)
+        t = read_floor(nb, clock)
         floors.append({"shape": name, "bytes": nb, "read_us": round(t * 1e6, 3), "GBps": round(nb / t / 1e9, 1)})
-    ctr = counters_for("tri_gemv.hip")
+    ctr = counters()
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(elapsed / args.steps * 1e3, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "accumulate": "f32", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
         "config": {"workload": "decode GEMV, M=1, 2-bit packed ternary weights, shapes 4096x4096 + 4096->11008 + "
-                               "11008->4096 per step, weights cold (rotating >= 1 GiB pool)",
+                               "11008->4096 per step, each matrix rotating over 64 copies (cold)",
                    "M": 1, "shapes": [[K, N] for (_, K, N) in dcfg["shapes"]], "format": "2bit",
-                   "bytes_per_step": step_bytes},
+                   "accumulate": "f32", "bytes_per_step": step_bytes, "timing": "HIP graph replay"},
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "kernel": "k_gemv2 (tri_gemv.hip)", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": (ctr or {}).get("traffic_bytes_per_step")},
+                     "traffic": (ctr or {}).get("traffic_bytes_per_step"),
+                     "algorithmic_bytes": step_bytes, "launches": len(per_launch),
+                     "mean_launch_us": round(sum(per_launch) / len(per_launch) * 1e6, 3), "queue_ahead": ahead},
         "per_shape": shapes_out,
         "read_floor": floors,
     }
     if not args.skip_extra:
-        out["batched"] = bench_batched()
-        out["prefill"] = bench_prefill()
+        out["batched"] = bench_batched(clock)
+        out["block"] = bench_block(clock)
+        out["prefill"] = bench_prefill(clock)
     if not args.skip_cpu:
         out["cpu_baseline"] = cpu_baseline(dcfg["shapes"])
     print(json.dumps(out), flush=True)
 
 
-def bench_batched():
+def bench_batched(clock):
     import torch
-    import bit_mixed_precision_tri_amd as tri
     from bit_mixed_precision_tri_amd import configs
     cfg = configs.BATCHED
     res = []
     for fmt in cfg["fmts"]:
         for li, (name, K, N) in enumerate(cfg["shapes"]):
             for M in cfg["Ms"]:
-                L = Layer(cfg["workload_id"], 10 * li + M, M, N, K, fmt)
-                t = time_launches(L, 100, 10)
+                L = Layer(cfg["workload_id"], 10 * li + M, M, N, K, fmt, copies=32)
+                t, _ = clock.run([L.launch] * 100)
                 res.append({"shape": name, "M": M, "format": configs.FMT_NAMES[fmt], "kernel_us": round(t * 1e6, 3),
                             "GBps": round(L.bytes / t / 1e9, 1), "frac_hbm": round(L.bytes / t / 1e9 / HBM_PEAK_GBS, 4)})
                 del L
@@ -256,15 +316,34 @@ def bench_batched():
     return res
 
 
-def bench_prefill():
+def bench_block(clock):
+    """The seven linears of one block decode step, back to back (inputs pre-staged)."""
+    import torch
+    from bit_mixed_precision_tri_amd import configs
+    cfg = configs.BLOCK
+    res = []
+    for M in cfg["Ms"]:
+        layers = [Layer(cfg["workload_id"], 100 * M + li, M, N, K, cfg["fmt"], copies=16)
+                  for li, (name, K, N) in enumerate(cfg["layers"])]
+        t, _ = clock.run([L.launch for _ in range(50) for L in layers])
+        tstep = t * len(layers)
+        nbytes = sum(L.bytes for L in layers)
+        res.append({"M": M, "launches": len(layers), "bytes": nbytes, "step_us": round(tstep * 1e6, 3),
+                    "GBps": round(nbytes / tstep / 1e9, 1), "frac_hbm": round(nbytes / tstep / 1e9 / HBM_PEAK_GBS, 4)})
+        del layers
+        torch.cuda.empty_cache()
+    return res
+
+
+def bench_prefill(clock):
     import torch
     from bit_mixed_precision_tri_amd import configs
     cfg = configs.PREFILL
     res = []
     for fmt in cfg["fmts"]:
         for li, (name, K, N) in enumerate(cfg["shapes"]):
-            L = Layer(cfg["workload_id"], li, cfg["M"], N, K, fmt, cfg["scale"], pool_bytes=0, max_copies=1)
-            t = time_launches(L, 10, 2)
+            L = Layer(cfg["workload_id"], li, cfg["M"], N, K, fmt, cfg["scale"], copies=1)
+            t, _ = clock.run([L.launch] * 12, warmup=2)
             tf = L.flops / t / 1e12
             res.append({"shape": name, "M": cfg["M"], "format": configs.FMT_NAMES[fmt], "kernel_us": round(t * 1e6, 2),
                         "TFLOPs": round(tf, 2), "frac_mfma": round(tf / MFMA_F16_PEAK_TFLOPS, 4)})
@@ -274,21 +353,17 @@ def bench_prefill():
 
 
 def profile_mode(which):
-    """Launch one workload a few times and exit (for rocprofv3 --kernel-trace / --pmc)."""
+    """Launch one workload a few times and exit (for rocprofv3 counter passes)."""
     import torch
     import bit_mixed_precision_tri_amd as tri
     from bit_mixed_precision_tri_amd import configs
-    F2 = tri.TRI_FMT_2BIT
     if which == "decode":
         cfg = configs.DECODE
-        layers = [Layer(cfg["workload_id"], li, 1, N, K, F2) for li, (name, K, N) in enumerate(cfg["shapes"])]
+        layers = [Layer(cfg["workload_id"], li, 1, N, K, tri.TRI_FMT_2BIT)
+                  for li, (name, K, N) in enumerate(cfg["shapes"])]
         for _ in range(20):
             for L in layers:
                 L.launch()
-    elif which == "batched":
-        return bench_batched()
-    elif which == "prefill":
-        return bench_prefill()
     elif which == "copy":
         nb = 64 << 20
         src = torch.ones(nb, dtype=torch.uint8, device="cuda")
