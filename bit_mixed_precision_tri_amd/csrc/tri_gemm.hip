@@ -74,20 +74,29 @@ __device__ __forceinline__ uint32_t digits_to_t(uint32_t w, uint32_t bias)
 }  // namespace
 
 constexpr int kBM = 128;             // rows of Y per workgroup
-constexpr int kNT = 4;               // 32-column MFMA tiles per wave
 constexpr int kMT = 4;               // 32-row MFMA tiles per wave
-constexpr int kBN = 4 * 32 * kNT;    // columns of Y per workgroup (4 waves side by side)
+constexpr int kBN = 512;             // columns of Y per tile (4 waves side by side, 4 MFMA tiles each)
+constexpr int kCUs = 256;            // workgroups the chip runs at once (one per CU)
 
-template <int FMT>
+// A workgroup computes one 128 x 512 tile of Y (NT = 4) or one half of it, 128 x 256 (NT = 2),
+// tile_base + blockIdx.x (NT = 4) or tile_base + blockIdx.x / 2 (NT = 2) in the tile order.
+template <int FMT, int NT>
 __global__ __launch_bounds__(256) void k_gemm(const uint16_t *__restrict__ X, const uint8_t *__restrict__ Wp,
                                               float scale, int M, int N, int K, int C, int tiles_m, int tiles_n,
-                                              uint16_t *__restrict__ Y)
+                                              int tile_base, uint16_t *__restrict__ Y)
 {
+    constexpr int kNT = NT;                      // 32-column MFMA tiles per wave
     constexpr bool TWO = FMT == TRI_FMT_2BIT;
     constexpr int BK = TWO ? 128 : 160;          // trits per K tile (32 packed bytes per weight row)
     constexpr int KS = BK / 16;                  // MFMA k-steps per K tile
     constexpr int ASTR = BK + 8;                 // LDS row stride in halves (16 bytes of padding)
-    constexpr int XP = BK / 8 / 2;               // 16-byte activation pieces per thread per K tile
+    // activation groups: the values whose weight trits share decode registers (16 for 2-bit,
+    // 40 for 1.6-bit); a thread loads whole groups, lanes walking along a row
+    constexpr int GV = TWO ? 16 : 40;            // values per group
+    constexpr int GPR = BK / GV;                 // groups per row and K tile (8 or 4)
+    constexpr int GP = GV / 8;                   // 16-byte pieces per group
+    constexpr int NG = kBM * GPR / 256;          // groups per thread and K tile
+    constexpr int XP = NG * GP;                  // 16-byte pieces per thread and K tile
     __shared__ uint16_t abuf[2][kBM * ASTR];
     __shared__ uint32_t lut[TWO ? 1 : 256];
 
@@ -97,23 +106,28 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t *__restrict__ X, co
     const int h = lane >> 5;
     const int c = lane & 31;
 
-    // XCD-aware tile order: workgroups are dealt round-robin over 8 XCDs; renumber so that
-    // the workgroups of one XCD are consecutive, then walk row tiles fastest.
-    const int nwg = tiles_m * tiles_n;
+    // Tile order.  Workgroups are dealt round-robin over the 8 XCDs; renumber them so that
+    // each XCD gets a contiguous range, and walk the tiles in bands of kGM row tiles: the 32
+    // workgroups an XCD runs at once then cover 4 row tiles x 8 column tiles and share
+    // activations and weights in that XCD's L2.
+    constexpr int kGM = 4;
+    const int nwg = gridDim.x;
     int bid = blockIdx.x;
     if ((nwg & 7) == 0) bid = (bid & 7) * (nwg >> 3) + (bid >> 3);
-    const int tm = bid % tiles_m;
-    const int tn = bid / tiles_m;
+    const int t = tile_base + (NT == 4 ? bid : bid >> 1);
+    const int band = t / (kGM * tiles_n);
+    const int first_m = band * kGM;
+    const int band_m = min(tiles_m - first_m, kGM);
+    const int in_band = t - band * kGM * tiles_n;
+    const int tm = first_m + in_band % band_m;
+    const int tn = in_band / band_m;
     const int m0 = tm * kBM;
-    const int n0 = tn * kBN + 32 * kNT * wv;     // this wave's first column
+    const int n0 = tn * kBN + (NT == 4 ? 0 : (bid & 1) * (kBN / 2)) + 32 * kNT * wv;   // this wave's first column
 
     if constexpr (!TWO) {
         lut[tid] = base3_digits_2bit((uint32_t)tid);   // 256 threads, one entry each
     }
 
-    // activations: thread -> (row tid/2, half ah = tid%2 of the K tile), XP 16-byte pieces
-    const int arow = tid >> 1;
-    const int ah = tid & 1;
     const uint32_t xbytes = __builtin_amdgcn_readfirstlane((uint32_t)((int64_t)min(kBM, M - m0) * K * 2));
     const __amdgpu_buffer_rsrc_t xr = rsrc(X + (int64_t)m0 * K, xbytes);
     // weights: lane (h, c) of column tile nt reads row n0 + 32nt + c, bytes 16h.. of each slice
@@ -126,14 +140,22 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t *__restrict__ X, co
     const __amdgpu_buffer_rsrc_t wr = rsrc(Wp + (int64_t)wrow * S, wbytes);
     const int KT = (C + 1) / 2;                  // K tiles (two 16-byte chunks each)
 
+    // Activations of K tile kt (tiles past the end read zeros: the k < K test and the
+    // buffer range check); group gi = q*256 + tid is group gi % GPR of row gi / GPR.
     auto load_a = [&](int kt, u32x4 (&xa)[XP]) {
 #pragma unroll
-        for (int q = 0; q < XP; ++q) {
-            const int k = kt * BK + ah * (BK / 2) + 8 * q;
-            const uint32_t off = (uint32_t)(arow * K + k) * 2u;
-            xa[q] = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)(k < K ? off : 0x80000000u), 0, 0);
+        for (int q = 0; q < NG; ++q) {
+            const int gi = q * 256 + tid;
+            const int row = gi / GPR, G = gi % GPR;
+#pragma unroll
+            for (int j = 0; j < GP; ++j) {
+                const int k = kt * BK + GV * G + 8 * j;
+                const uint32_t off = (uint32_t)(row * K + k) * 2u;
+                xa[q * GP + j] = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)(k < K ? off : 0x80000000u), 0, 0);
+            }
         }
     };
+    // Weights of K tile kt (a tile past the end reads bytes that are never used, within range).
     auto load_b = [&](int kt, u32x4 (&wb)[kNT]) {
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) {
@@ -141,41 +163,47 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t *__restrict__ X, co
             wb[nt] = __builtin_amdgcn_raw_buffer_load_b128(wr, (int)off, 0, 0);
         }
     };
-    // Permute this thread's half row of activations into the pairing of the decoded weights
-    // and store it in k-step order: the values of k-step s for lane half ah sit at 16s + 8ah.
+    // Permute each group into the pairing of the decoded weights and store it in k-step
+    // order: the 8 values lane half hh uses at k-step s sit at 16s + 8hh of the row.
     auto store_a = [&](int buf, const u32x4 (&xa)[XP]) {
-        uint16_t *dst = &abuf[buf][arow * ASTR + 8 * ah];
-        uint32_t v[XP * 4];
 #pragma unroll
-        for (int q = 0; q < XP; ++q) {
-            v[4 * q] = xa[q][0]; v[4 * q + 1] = xa[q][1]; v[4 * q + 2] = xa[q][2]; v[4 * q + 3] = xa[q][3];
-        }
-        uint32_t o[XP * 4];
-        if constexpr (TWO) {
-            // each 16-value group q: (x0,x8),(x1,x9),...,(x7,x15); k-steps 2q and 2q+1
+        for (int q = 0; q < NG; ++q) {
+            const int gi = q * 256 + tid;
+            const int row = gi / GPR, G = gi % GPR;
+            uint32_t v[GV / 2];
 #pragma unroll
-            for (int w = 0; w < XP * 4 / 8; ++w)
+            for (int j = 0; j < GP; ++j) {
+                v[4 * j] = xa[q * GP + j][0]; v[4 * j + 1] = xa[q * GP + j][1];
+                v[4 * j + 2] = xa[q * GP + j][2]; v[4 * j + 3] = xa[q * GP + j][3];
+            }
+            uint16_t *rowp = &abuf[buf][row * ASTR];
+            if constexpr (TWO) {
+                // group G = 4hh + qq: pairs (x_p, x_{p+8}); p = 0..3 feed k-step 2qq, p = 4..7 k-step 2qq+1
+                const int hh = G >> 2, qq = G & 3;
+                uint32_t o[8];
 #pragma unroll
                 for (int p = 0; p < 8; p += 2) {
-                    o[8 * w + p] = pair_halves<0>(v[8 * w + 4 + p / 2], v[8 * w + p / 2]);
-                    o[8 * w + p + 1] = pair_halves<1>(v[8 * w + 4 + p / 2], v[8 * w + p / 2]);
+                    o[p] = pair_halves<0>(v[4 + p / 2], v[p / 2]);
+                    o[p + 1] = pair_halves<1>(v[4 + p / 2], v[p / 2]);
                 }
-        } else {
-            // each 40-value group gg: for p = 0..4, r = 0..3: (x[5r+p], x[5r+20+p]); k-steps 5gg+p
+                *reinterpret_cast<u32x4 *>(rowp + 16 * (2 * qq) + 8 * hh) = u32x4{o[0], o[1], o[2], o[3]};
+                *reinterpret_cast<u32x4 *>(rowp + 16 * (2 * qq + 1) + 8 * hh) = u32x4{o[4], o[5], o[6], o[7]};
+            } else {
+                // group G = 2hh + g5: for p = 0..4, r = 0..3: (x[5r+p], x[5r+20+p]) feed k-step 5g5+p
+                const int hh = G >> 1, g5 = G & 1;
 #pragma unroll
-            for (int gg = 0; gg < XP * 4 / 20; ++gg)
-#pragma unroll
-                for (int p = 0; p < 5; ++p)
+                for (int p = 0; p < 5; ++p) {
+                    uint32_t o[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int e = 5 * r + p;           // value index in the group; partner e + 20
-                        o[20 * gg + 4 * p + r] = (e & 1) ? pair_halves<1>(v[20 * gg + (e >> 1) + 10], v[20 * gg + (e >> 1)])
-                                                         : pair_halves<0>(v[20 * gg + (e >> 1) + 10], v[20 * gg + (e >> 1)]);
+                        const int e = 5 * r + p;   // value index in the group; partner e + 20
+                        o[r] = (e & 1) ? pair_halves<1>(v[(e >> 1) + 10], v[e >> 1])
+                                       : pair_halves<0>(v[(e >> 1) + 10], v[e >> 1]);
                     }
+                    *reinterpret_cast<u32x4 *>(rowp + 16 * (5 * g5 + p) + 8 * hh) = u32x4{o[0], o[1], o[2], o[3]};
+                }
+            }
         }
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-            *reinterpret_cast<u32x4 *>(dst + 16 * s) = u32x4{o[4 * s], o[4 * s + 1], o[4 * s + 2], o[4 * s + 3]};
     };
 
     float16_t acc[kMT][kNT];
@@ -186,62 +214,61 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t *__restrict__ X, co
     uint32_t bias;
     asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(bias));   // register-held constant (no memory access)
 
-    // Weight source registers of the current K tile: the packed dwords (2-bit) or the digit
-    // codes of byte pairs (b, b + 4) of each 8-byte half (1.6-bit).
-    constexpr int SW = TWO ? 4 : 8;
-    uint32_t src[kNT][SW];
-    u32x4 xa[XP];
-    u32x4 wn[kNT];
-    auto take_b = [&]() {
+    // 1.6-bit: digit codes of byte pairs (b, b + 4) of each 8-byte half of the lane's 16 bytes
+    uint32_t code[kNT][TWO ? 1 : 8];
+    auto take_codes = [&](const u32x4 (&wb)[kNT]) {
+        if constexpr (!TWO) {
 #pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) {
-            if constexpr (TWO) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) src[nt][q] = wn[nt][q];
-            } else {
+            for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
                 for (int cc = 0; cc < 8; ++cc) {
-                    const uint32_t lo = wn[nt][2 * (cc >> 2)], hi = wn[nt][2 * (cc >> 2) + 1];
+                    const uint32_t lo = wb[nt][2 * (cc >> 2)], hi = wb[nt][2 * (cc >> 2) + 1];
                     const int sh = 8 * (cc & 3);
-                    src[nt][cc] = lut[(lo >> sh) & 0xFFu] | (lut[(hi >> sh) & 0xFFu] << 16);
+                    code[nt][cc] = lut[(lo >> sh) & 0xFFu] | (lut[(hi >> sh) & 0xFFu] << 16);
                 }
-            }
         }
     };
-    // B operand of k-step s, column tile nt
-    auto decode = [&](int s, int nt) {
+    // B operand of k-step s, column tile nt (2-bit: from the packed words; 1.6-bit: from the codes)
+    auto decode = [&](const u32x4 (&wb)[kNT], int s, int nt) {
         u32x4 b;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             if constexpr (TWO)
-                b[r] = digits_to_t(src[nt][s >> 1] >> (2 * (4 * (s & 1) + r)), bias);
+                b[r] = digits_to_t(wb[nt][s >> 1] >> (2 * (4 * (s & 1) + r)), bias);
             else
-                b[r] = digits_to_t(src[nt][4 * (s / 5) + r] >> (2 * (s % 5)), bias);
+                b[r] = digits_to_t(code[nt][4 * (s / 5) + r] >> (2 * (s % 5)), bias);
         }
         return b;
     };
 
+    // Two weight register sets alternate between K tiles (the loop below is unrolled by two so
+    // the alternation costs no copies): a tile decodes from one while the next tile's words
+    // arrive in the other.  The activations of tile kt + 2 are loaded right after tile kt + 1's
+    // are staged, so every load has about one K tile of MFMA work to arrive.
+    u32x4 xa[XP];
+    u32x4 w0[kNT], w1[kNT];
+    // (loads are issued in the loop's order -- activations, then weights -- so the wait
+    // counts the compiler derives at the loop entry match those of the loop itself)
     load_a(0, xa);
-    load_b(0, wn);
+    load_b(0, w0);
     store_a(0, xa);
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(1, xa);
+    load_b(1, w1);
     __syncthreads();                             // tile 0's activations and the byte table
-    take_b();
+    take_codes(w0);
     const int aoff = c * ASTR + 8 * h;
     u32x4 afr[kMT], bop[kNT];
 #pragma unroll
     for (int mt = 0; mt < kMT; ++mt) afr[mt] = *reinterpret_cast<const u32x4 *>(&abuf[0][aoff + 32 * mt * ASTR]);
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) bop[nt] = decode(0, nt);
+    for (int nt = 0; nt < kNT; ++nt) bop[nt] = decode(w0, 0, nt);
 
-    // One K tile; MORE (a compile-time flag, so the tile body has no branches) says whether a
-    // next tile exists.
-    auto tile = [&](int kt, auto more_tag) {
+    // One K tile: wc holds its weights, wx those of the next tile.  MORE (compile-time, so the
+    // tile body has no branches) says whether a next tile exists.
+    auto tile = [&](int kt, auto more_tag, u32x4 (&wc)[kNT], u32x4 (&wx)[kNT]) __attribute__((always_inline)) {
         constexpr bool MORE = decltype(more_tag)::value;
         const int buf = kt & 1;
-        if constexpr (MORE) {
-            load_a(kt + 1, xa);
-            load_b(kt + 1, wn);
-        }
         const uint16_t *acur = &abuf[buf][aoff];
         const uint16_t *anext = &abuf[buf ^ 1][aoff];
 #pragma unroll
@@ -255,13 +282,13 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t *__restrict__ X, co
                 for (int mt = 0; mt < kMT; ++mt)
                     an[mt] = *reinterpret_cast<const u32x4 *>(acur + 32 * mt * ASTR + 16 * (s + 1));
 #pragma unroll
-                for (int nt = 0; nt < kNT; ++nt) bn[nt] = decode(s + 1, nt);
+                for (int nt = 0; nt < kNT; ++nt) bn[nt] = decode(wc, s + 1, nt);
             } else if (MORE) {
 #pragma unroll
                 for (int mt = 0; mt < kMT; ++mt) an[mt] = *reinterpret_cast<const u32x4 *>(anext + 32 * mt * ASTR);
-                take_b();                        // the last decode of this tile's words was at step KS - 2
+                take_codes(wx);                  // the last decode of this tile's codes was at step KS - 2
 #pragma unroll
-                for (int nt = 0; nt < kNT; ++nt) bn[nt] = decode(0, nt);
+                for (int nt = 0; nt < kNT; ++nt) bn[nt] = decode(wx, 0, nt);
             }
 #pragma unroll
             for (int mt = 0; mt < kMT; ++mt)
@@ -276,6 +303,8 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t *__restrict__ X, co
                 if (i % 4 == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
             }
             __builtin_amdgcn_sched_barrier(0);
+            if (MORE && s == KS - 2) load_a(kt + 2, xa);   // past the last tile: zeros, never stored
+            if (MORE && s == KS - 1) load_b(kt + 2, wc);   // wc's last decode was at step KS - 2
             if (s + 1 < KS || MORE) {
 #pragma unroll
                 for (int mt = 0; mt < kMT; ++mt) afr[mt] = an[mt];
@@ -284,8 +313,15 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t *__restrict__ X, co
             }
         }
     };
-    for (int kt = 0; kt + 1 < KT; ++kt) tile(kt, std::true_type{});
-    tile(KT - 1, std::false_type{});
+    // An even number of tiles keeps a single code path: an odd count gets one more tile past
+    // the end, whose activations read as zero, so it adds exact zeros.
+    const int KTe = (KT + 1) & ~1;
+    for (int kt = 0; kt + 2 < KTe; kt += 2) {
+        tile(kt, std::true_type{}, w0, w1);
+        tile(kt + 1, std::true_type{}, w1, w0);
+    }
+    tile(KTe - 2, std::true_type{}, w0, w1);
+    tile(KTe - 1, std::false_type{}, w1, w0);
 
     // epilogue: lane (h, c) holds rows 32mt + 8i + 4h + v of column 32nt + c
 #pragma unroll
@@ -304,6 +340,28 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t *__restrict__ X, co
         }
 }
 
+template <int FMT>
+static int launch_fmt(const uint16_t *X, const uint8_t *Wp, float scale, int M, int N, int K, int C, uint16_t *Y,
+                      hipStream_t s)
+{
+    const int tiles_m = (M + kBM - 1) / kBM;
+    const int tiles_n = (N + kBN - 1) / kBN;
+    const int64_t T = (int64_t)tiles_m * tiles_n;
+    if (T >= ((int64_t)1 << 30)) return TRI_EINVAL;
+    // A last round of full tiles that would leave more than half of the CUs idle is run as
+    // twice as many half-width tiles instead, by a second launch.
+    const int r = (int)(T % kCUs);
+    const int tail = (r > 0 && r <= kCUs / 2) ? r : 0;
+    const int full = (int)T - tail;
+    if (full > 0)
+        hipLaunchKernelGGL((k_gemm<FMT, 4>), dim3((unsigned)full), dim3(256), 0, s, X, Wp, scale, M, N, K, C, tiles_m,
+                           tiles_n, 0, Y);
+    if (tail > 0)
+        hipLaunchKernelGGL((k_gemm<FMT, 2>), dim3((unsigned)(2 * tail)), dim3(256), 0, s, X, Wp, scale, M, N, K, C,
+                           tiles_m, tiles_n, full, Y);
+    return hipGetLastError() == hipSuccess ? TRI_OK : TRI_EHIP;
+}
+
 int launch_gemm(const uint16_t *X, const uint8_t *Wp, float scale, int64_t M, int N, int K, int fmt, uint16_t *Y,
                 hipStream_t s)
 {
@@ -312,7 +370,7 @@ int launch_gemm(const uint16_t *X, const uint8_t *Wp, float scale, int64_t M, in
     // 32-bit buffer offsets: a 128-row activation block and a 128-row weight block must stay
     // below 2^31 bytes, and activations are read in pieces of 8 values (K % 8 == 0).  Other
     // shapes run the small-M kernels over 16-row slices of X.
-    const bool fits = (K % 8) == 0 && (int64_t)kBM * K * 2 < ((int64_t)1 << 31) && 32 * kNT * S < ((int64_t)1 << 31);
+    const bool fits = (K % 8) == 0 && (int64_t)kBM * K * 2 < ((int64_t)1 << 31) && 128 * S < ((int64_t)1 << 31);
     if (!fits) {
         for (int64_t m0 = 0; m0 < M; m0 += 16) {
             const int mm = (int)((M - m0) < 16 ? (M - m0) : 16);
@@ -321,19 +379,11 @@ int launch_gemm(const uint16_t *X, const uint8_t *Wp, float scale, int64_t M, in
         }
         return TRI_OK;
     }
-    for (int64_t mb = 0; mb < M; mb += (int64_t)1 << 24) {   // grid.x limit: 2^24 row tiles per launch
-        const int mm = (int)((M - mb) < ((int64_t)1 << 24) ? (M - mb) : ((int64_t)1 << 24));
-        const int tiles_m = (mm + kBM - 1) / kBM;
-        const int tiles_n = (N + kBN - 1) / kBN;
-        const int64_t nwg = (int64_t)tiles_m * tiles_n;
-        if (nwg >= ((int64_t)1 << 31)) return TRI_EINVAL;
-        if (fmt == TRI_FMT_2BIT)
-            hipLaunchKernelGGL(k_gemm<TRI_FMT_2BIT>, dim3((unsigned)nwg), dim3(256), 0, s, X + mb * K, Wp, scale, mm,
-                               N, K, C, tiles_m, tiles_n, Y + mb * N);
-        else
-            hipLaunchKernelGGL(k_gemm<TRI_FMT_1P6BIT>, dim3((unsigned)nwg), dim3(256), 0, s, X + mb * K, Wp, scale,
-                               mm, N, K, C, tiles_m, tiles_n, Y + mb * N);
-        if (hipGetLastError() != hipSuccess) return TRI_EHIP;
+    for (int64_t mb = 0; mb < M; mb += (int64_t)1 << 20) {   // keeps the tile count of a launch in int range
+        const int mm = (int)((M - mb) < ((int64_t)1 << 20) ? (M - mb) : ((int64_t)1 << 20));
+        const int rc = fmt == TRI_FMT_2BIT ? launch_fmt<TRI_FMT_2BIT>(X + mb * K, Wp, scale, mm, N, K, C, Y + mb * N, s)
+                                           : launch_fmt<TRI_FMT_1P6BIT>(X + mb * K, Wp, scale, mm, N, K, C, Y + mb * N, s);
+        if (rc != TRI_OK) return rc;
     }
     return TRI_OK;
 }

@@ -280,3 +280,20 @@ def test_prefill_full_size_sampled_rows(fmt, li):
     say("  worst err/tol %.3g, fraction equal to fp16(ref) %.3f" % (worst, exact))
     del Wp
     torch.cuda.empty_cache()
+
+
+# Full-width GEMM tiles (128 x 512) with ragged edges in M and N and an odd number of K tiles:
+# 8 x 32 = 256 tiles, so no half-width tail launch; sampled rows include the last partial tile.
+GEMM_EDGE_ROWS = [0, 1, 127, 128, 500, 895, 896, 997, 998, 999]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemm_full_tiles_ragged_edges(fmt):
+    M, N, K = 1000, 16000, 328
+    W, X, s = synth.layer_inputs(300 + fmt, 1, M, N, K)
+    Wp = tri.pack(cuda(W), fmt)
+    say("gemm full tiles M=%d N=%d K=%d fmt=%d" % (M, N, K, fmt))
+    Y = run_layer(X, Wp, s, K, fmt, tri.TRI_ALGO_GEMM)
+    assert np.all(np.isfinite(Y))
+    worst, exact = check_layer(Y, X, W, s, "gemm edges fmt=%d" % fmt, rows=GEMM_EDGE_ROWS)
+    say("  worst err/tol %.3g, fraction equal to fp16(ref) %.3f" % (worst, exact))
