@@ -27,8 +27,7 @@ int check_linear(const void *X, const void *Wp, int64_t M, int64_t N, int64_t K,
 
 int select_algo(int64_t M, int fmt)
 {
-    if (M == 1 && fmt == TRI_FMT_2BIT) return TRI_ALGO_GEMV;
-    if (M <= 16) return TRI_ALGO_SMALLM;
+    if (M <= 16) return TRI_ALGO_SMALLM;          // (at M = 1 the MFMA kernel beats the VALU GEMV)
     return TRI_ALGO_GEMM;
 }
 

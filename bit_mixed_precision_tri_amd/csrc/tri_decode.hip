@@ -229,168 +229,12 @@ __global__ __launch_bounds__(64 * NW) void k_decode(const uint16_t *__restrict__
 // them into the A-operand order and writes them; after that only the final tile reduction
 // synchronises the workgroup.  A rows 1..15 (lanes j > 0) read the same staged row: their
 // tile rows are never stored.
-template <int FMT, int NW, int CST>
-__global__ __launch_bounds__(64 * NW) void k_decode_m1(const uint16_t *__restrict__ X, const uint8_t *__restrict__ Wp,
-                                                       float scale, int N, int K, int C, uint16_t *__restrict__ Y)
-{
-    constexpr bool TWO = FMT == TRI_FMT_2BIT;
-    constexpr int NPOS = TWO ? 8 : 10;
-    constexpr int NCLS = TWO ? 6 : 5;
-    constexpr int XH = TWO ? 64 : 80;
-    static_assert(4 * CST <= 64, "one staging item per lane");
-    __shared__ u32x4 xa[NW][4 * CST * NPOS];   // per wave: [local chunk][operand]
-    __shared__ uint32_t lut[TWO ? 1 : 256];
-    __shared__ float red[NW][16];
-
-    const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6;
-    const int g = lane >> 4;
-    const int j = lane & 15;
-    const int n0 = blockIdx.x * 15;
-    const int64_t S = (int64_t)C * 16;
-
-    if constexpr (!TWO) {
-        for (int b = threadIdx.x; b < 256; b += 64 * NW) lut[b] = base3_digits_2bit((uint32_t)b);
-    }
-
-    // (1) this lane's staging item: local chunk l = lane (if l < 4*CST)
-    const int ls = lane >> 2, lg = lane & 3;
-    const int lc = 4 * (ls * NW + wv) + lg;       // global chunk of the item
-    const bool item = lane < 4 * CST;
-    const __amdgpu_buffer_rsrc_t x_rsrc = buffer_rsrc(X, (uint32_t)K * 2u);
-    u32x4 xr[XH / 8];
-#pragma unroll
-    for (int q = 0; q < XH / 8; ++q) {
-        const int k = lc * XH + 8 * q;
-        xr[q] = buffer_ld16(x_rsrc, (item && k < K) ? (uint32_t)k * 2u : 0x80000000u, 0);
-    }
-    // (2) every weight chunk of this wave (rows past N and bytes past the matrix read zero)
-    const int rows_here = min(15, N - n0);
-    const __amdgpu_buffer_rsrc_t w_rsrc = buffer_rsrc(Wp + n0 * S, (uint32_t)(rows_here * S));
-    const uint32_t wbase = j < 15 ? (uint32_t)(j * S + (4 * wv + g) * 16) : 0x80000000u;
-    u32x4 wq[CST];
-#pragma unroll
-    for (int s = 0; s < CST; ++s) wq[s] = buffer_ld16(w_rsrc, wbase + (uint32_t)(s * 64 * NW), 0);
-    const uint32_t zfill = j == 15 ? (TWO ? 0x55555555u : 0x79797979u) : 0u;
-
-    // (3) stage the item (wave-local: LDS operations of one wave complete in order)
-    if (item) {
-        uint32_t x32[XH / 2];
-#pragma unroll
-        for (int q = 0; q < XH / 8; ++q) {
-            x32[4 * q] = xr[q][0]; x32[4 * q + 1] = xr[q][1]; x32[4 * q + 2] = xr[q][2]; x32[4 * q + 3] = xr[q][3];
-        }
-        u32x4 *dst = &xa[wv][lane * NPOS];
-        if constexpr (TWO) {
-#pragma unroll
-            for (int p = 0; p < 8; ++p) {
-                u32x4 a;
-#pragma unroll
-                for (int w = 0; w < 4; ++w)
-                    a[w] = (p & 1) ? pair_halves<1>(x32[8 * w + 4 + p / 2], x32[8 * w + p / 2])
-                                   : pair_halves<0>(x32[8 * w + 4 + p / 2], x32[8 * w + p / 2]);
-                dst[p] = a;
-            }
-        } else {
-#pragma unroll
-            for (int p = 0; p < 5; ++p)
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    u32x4 a;
-#pragma unroll
-                    for (int qq = 0; qq < 4; ++qq) {
-                        const int e = 5 * (4 * h + qq) + p;
-                        a[qq] = (e & 1) ? pair_halves<1>(x32[(e >> 1) + 20], x32[e >> 1])
-                                        : pair_halves<0>(x32[(e >> 1) + 20], x32[e >> 1]);
-                    }
-                    dst[2 * p + h] = a;
-                }
-        }
-    }
-    if constexpr (!TWO) __syncthreads();          // the byte table is shared by the workgroup
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // (4) decode and contract
-    const float4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-    float4_t acc[NCLS];
-#pragma unroll
-    for (int c = 0; c < NCLS; ++c) acc[c] = zero4;
-#pragma unroll
-    for (int s = 0; s < CST; ++s) {
-        if (4 * (s * NW + wv) >= C) break;       // wave-uniform: no chunk of this step is live
-        const u32x4 *asrc = &xa[wv][(4 * s + g) * NPOS];
-        const u32x4 v = wq[s] | zfill;
-        if constexpr (TWO) {
-            const u32x4 u = v >> 12u;
-#pragma unroll
-            for (int p = 0; p < 6; ++p) acc[p] = mfma(asrc[p], v & (0x00030003u << (2 * p)), acc[p]);
-            acc[0] = mfma(asrc[6], u & 0x00030003u, acc[0]);
-            acc[1] = mfma(asrc[7], u & 0x000C000Cu, acc[1]);
-        } else {
-            u32x4 lo, hi;
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const uint32_t blo = (v[q >> 2] >> (8 * (q & 3))) & 0xFFu;
-                const uint32_t bhi = (v[2 + (q >> 2)] >> (8 * (q & 3))) & 0xFFu;
-                const uint32_t pq = lut[blo] | (lut[bhi] << 16);
-                if (q < 4) lo[q] = pq; else hi[q - 4] = pq;
-            }
-#pragma unroll
-            for (int p = 0; p < 5; ++p) {
-                const uint32_t m = 0x00030003u << (2 * p);
-                acc[p] = mfma(asrc[2 * p], lo & m, acc[p]);
-                acc[p] = mfma(asrc[2 * p + 1], hi & m, acc[p]);
-            }
-        }
-    }
-
-    // (5) merge classes, sum the waves' row-0 tiles in a fixed order, subtract column 15
-    float4_t t = acc[0] + 0.25f * acc[1];
-    t += 0.0625f * acc[2] + 0.015625f * acc[3];
-    t += 0.00390625f * acc[4];
-    if constexpr (TWO) t += 0.0009765625f * acc[5];
-    if (g == 0) red[wv][j] = t[0];                // tile row 0 lives in lanes 0..15, element 0
-    __syncthreads();
-    if (threadIdx.x < 15 && n0 + (int)threadIdx.x < N) {
-        float sw = 0.f, sz = 0.f;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            sw += red[w][threadIdx.x];
-            sz += red[w][15];
-        }
-        Y[n0 + threadIdx.x] = __builtin_bit_cast(uint16_t, (_Float16)(((sw - sz) * 16777216.0f) * scale));
-    }
-}
-
-template <int FMT, int NW, int CST>
-static void launch_dec_m1(const uint16_t *X, const uint8_t *Wp, float scale, int N, int K, int C, uint16_t *Y,
-                          hipStream_t s)
-{
-    hipLaunchKernelGGL((k_decode_m1<FMT, NW, CST>), dim3((N + 14) / 15), dim3(64 * NW), 0, s, X, Wp, scale, N, K, C,
-                       Y);
-}
-
 template <int FMT, int MT, int NW, int CST, int GS>
 static void launch_dec(const uint16_t *X, const uint8_t *Wp, float scale, int M, int N, int K, int C, uint16_t *Y,
                        hipStream_t s)
 {
     hipLaunchKernelGGL((k_decode<FMT, MT, NW, CST, GS>), dim3((N + 14) / 15), dim3(64 * NW), 0, s, X, Wp, scale, M, N,
                        K, C, Y);
-}
-
-// M = 1 (1.6-bit; the 2-bit format uses the VALU GEMV): per-wave staging.
-template <int FMT>
-static bool launch_m1(const uint16_t *X, const uint8_t *Wp, float scale, int N, int K, int C, uint16_t *Y,
-                      hipStream_t s)
-{
-    if (C <= 32) launch_dec_m1<FMT, 2, 4>(X, Wp, scale, N, K, C, Y, s);
-    else if (C <= 64) launch_dec_m1<FMT, 4, 4>(X, Wp, scale, N, K, C, Y, s);
-    else if (C <= 160) launch_dec_m1<FMT, 8, 5>(X, Wp, scale, N, K, C, Y, s);
-    else if (C <= 256) launch_dec_m1<FMT, 16, 4>(X, Wp, scale, N, K, C, Y, s);
-    else return false;
-    return true;
 }
 
 // 2 <= M <= 16 with short rows: activations staged per workgroup, a few chunk-steps at a time.
@@ -414,9 +258,7 @@ bool launch_decode(const uint16_t *X, const uint8_t *Wp, float scale, int M, int
     // the activation pieces are 8 values wide, so K must be a multiple of 8
     if ((K % 8) != 0 || (int64_t)M * K * 2 >= ((int64_t)1 << 31) || 15 * (int64_t)C * 16 >= ((int64_t)1 << 31))
         return false;
-    if (M == 1)
-        return fmt == TRI_FMT_2BIT ? launch_m1<TRI_FMT_2BIT>(X, Wp, scale, N, K, C, Y, s)
-                                   : launch_m1<TRI_FMT_1P6BIT>(X, Wp, scale, N, K, C, Y, s);
+    if (M == 1) return launch_mv1(X, Wp, scale, N, K, fmt, Y, s);
     return fmt == TRI_FMT_2BIT ? launch_mn<TRI_FMT_2BIT>(X, Wp, scale, M, N, K, C, Y, s)
                                : launch_mn<TRI_FMT_1P6BIT>(X, Wp, scale, M, N, K, C, Y, s);
 }

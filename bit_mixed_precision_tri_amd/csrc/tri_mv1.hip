@@ -1,0 +1,274 @@
+// tri_mv1.hip -- ternary linear layer for one activation row (M = 1, decode) on MFMA.
+//
+// The layer (Pith review of "Spectra 1.1", "What carries the argument"):
+//   y[n] = scale * sum_k t[n][k] * x[k],  t in {-1, 0, +1},  fp32 accumulation.
+// At M = 1 the work is a matrix-vector product bound by the weight stream.  It still runs on
+// v_mfma_f32_16x16x32_f16: sixteen weight rows form the 16 columns of the B operand and the
+// activation chunk is broadcast to the 16 rows of A (only one output row is kept).  That
+// wastes matrix-core work but moves the multiply-adds off the vector ALU, which then only
+// masks the packed words -- one instruction per register, against one per trit on the VALU
+// path -- so the decode keeps pace with HBM.
+//
+// Decode.  Masking a packed register leaves each trit's digit d = t + 1 in the low bits of
+// an fp16 half, which reads exactly as d * 4^p * 2^-24 (p = the digit's position in its
+// 16-bit half): fp16 subnormals, or the two lowest exponent bits for p = 5.  One MFMA only
+// mixes digits of one position, so it accumulates exact products into one accumulator per
+// position class, and the classes are merged with exact powers of two.  That gives
+// sum_k d*x; since t = d - 1, sum_k x is subtracted once per row at the end.
+//   2-bit:   a register pairs trits (16v+p, 16v+8+p); positions 6, 7 are taken from the
+//            word shifted right by 12, so they share the classes of 0 and 1.
+//   1.6-bit: each byte goes through a 256-entry LDS table to its five base-3 digits at bits
+//            2j (the repeated division b'_i -> x_i that the review's referee report
+//            describes for the paper's section 3.2), and bytes q and q+8 of a chunk share a
+//            register: position p pairs trits (5q+p, 5q+40+p).
+// The sum over k is order-free, so the activations are permuted into the same pairing.
+//
+// Work split.  A workgroup of NW waves owns 16 weight rows; wave w takes chunk-steps s,
+// where lane (g = lane/16, j = lane%16) reads 16-byte chunk 4*(s*NW + w) + g of row j.  Every
+// weight chunk of the wave is requested at the start (reads past the matrix return zero;
+// chunks past a row's end meet zero activations).  The wave loads the activations of its own
+// chunks with whole-line loads, permutes them into the A-operand order in LDS (no
+// workgroup barrier), and adds them up for sum_k x.  The waves' partial sums meet in LDS and
+// are added in a fixed order (no atomics).
+#include "tri_device.h"
+#include "tri_internal.h"
+
+namespace tri {
+
+namespace {
+
+constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer resource, gfx9 family
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, (int)kRsrcWord3);
+}
+
+__device__ __forceinline__ float4_t mfma(const u32x4 a, const u32x4 b, float4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), c, 0,
+                                                  0, 0);
+}
+
+}  // namespace
+
+template <int FMT, int NW, int CST>
+__global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X, const uint8_t *__restrict__ Wp,
+                                                 float scale, int N, int K, int C, uint16_t *__restrict__ Y)
+{
+    constexpr bool TWO = FMT == TRI_FMT_2BIT;
+    constexpr int XH = TWO ? 64 : 80;            // activations per chunk
+    constexpr int NOP = TWO ? 8 : 10;            // A operands (MFMAs) per chunk
+    constexpr int NCLS = TWO ? 6 : 5;            // position classes
+    constexpr int NCH = 4 * CST;                 // chunks per wave
+    constexpr int PIECES = XH / 8;               // 16-byte activation pieces per chunk
+    constexpr int NLD = (NCH * PIECES + 63) / 64;   // whole-line activation loads per lane
+    static_assert(NCH <= 64, "chunks per wave");
+    __shared__ u32x4 xa[NW][NCH][NOP];           // per wave: A operands of its chunks
+    __shared__ u32x4 xraw[TWO ? 1 : NW][TWO ? 1 : NCH * PIECES];   // 1.6-bit: raw pieces
+    __shared__ uint32_t lut[TWO ? 1 : 256];
+    __shared__ float red[NW][17];
+
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar descriptors)
+    const int g = lane >> 4;
+    const int j = lane & 15;
+    const int n0 = blockIdx.x * 16;
+    const int64_t S = (int64_t)C * 16;
+
+    if constexpr (!TWO) {
+        for (int b = threadIdx.x; b < 256; b += 64 * NW) lut[b] = base3_digits_2bit((uint32_t)b);
+    }
+
+    // (1) activations of this wave's chunks: local chunk l is global chunk
+    //     4*((l/4)*NW + w) + l%4; piece P = 64i + lane of the wave's pieces is piece P % PIECES
+    //     of local chunk P / PIECES, so a load instruction reads whole 128-byte lines
+    const __amdgpu_buffer_rsrc_t xr = rsrc(X, (uint32_t)K * 2u);
+    u32x4 xv[NLD];
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+        const int P = 64 * i + lane;
+        const int l = P / PIECES;
+        const int gc = 4 * ((l >> 2) * NW + wv) + (l & 3);
+        const int k = gc * XH + 8 * (P % PIECES);
+        xv[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)((l < NCH && k < K) ? (uint32_t)k * 2u : 0x80000000u),
+                                                      0, 0);
+    }
+    // (2) every weight chunk of the wave, all in flight at once
+    const int rows_here = min(16, N - n0);
+    const __amdgpu_buffer_rsrc_t wr =
+        rsrc(Wp + (int64_t)n0 * S, __builtin_amdgcn_readfirstlane((uint32_t)(rows_here * S)));
+    u32x4 wq[CST];
+#pragma unroll
+    for (int s = 0; s < CST; ++s) {
+        const int c = 4 * (s * NW + wv) + g;
+        wq[s] = __builtin_amdgcn_raw_buffer_load_b128(wr, (int)(c < C ? (uint32_t)(j * S + c * 16) : 0x80000000u), 0, 0);
+    }
+
+    // (3) A operands in LDS, and this lane's share of sum_k x
+    float xsum = 0.f;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xsum = dot2(xv[i][e], 0x3C003C00u, xsum);   // (x_lo, x_hi) . (1, 1)
+    if constexpr (TWO) {
+        // lanes 2v, 2v+1 of a chunk's eight hold x[16v .. 16v+7] and x[16v+8 .. 16v+15]: they swap
+        // pieces (DPP quad_perm [1,0,3,2]); the even lane forms positions 0..3, the odd one 4..7
+        const bool odd = lane & 1;
+        const int vv = (lane & 7) >> 1;
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            const int l = (64 * i + lane) / PIECES;
+            u32x4 other;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) other[e] = (uint32_t)__builtin_amdgcn_mov_dpp((int)xv[i][e], 0xB1, 0xF, 0xF, false);
+            const u32x4 lo = odd ? other : xv[i];
+            const u32x4 hi = odd ? xv[i] : other;
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) {
+                const uint32_t dlo = odd ? lo[2 + pp / 2] : lo[pp / 2];
+                const uint32_t dhi = odd ? hi[2 + pp / 2] : hi[pp / 2];
+                const uint32_t r = (pp & 1) ? pair_halves<1>(dhi, dlo) : pair_halves<0>(dhi, dlo);
+                if (l < NCH) reinterpret_cast<uint32_t *>(&xa[wv][l][pp + (odd ? 4 : 0)])[vv] = r;
+            }
+        }
+    } else {
+        // the pairing of a 40-value half spans ten pieces: bounce the raw pieces through LDS
+#pragma unroll
+        for (int i = 0; i < NLD; ++i)
+            if (64 * i + lane < NCH * PIECES) xraw[wv][64 * i + lane] = xv[i];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (lane < NCH) {
+            uint32_t x32[40];
+#pragma unroll
+            for (int q = 0; q < 10; ++q) {
+                const u32x4 v = xraw[wv][10 * lane + q];
+                x32[4 * q] = v[0]; x32[4 * q + 1] = v[1]; x32[4 * q + 2] = v[2]; x32[4 * q + 3] = v[3];
+            }
+#pragma unroll
+            for (int p = 0; p < 5; ++p)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    u32x4 a;
+#pragma unroll
+                    for (int qq = 0; qq < 4; ++qq) {
+                        const int e = 5 * (4 * hh + qq) + p;   // value index; partner e + 40
+                        a[qq] = (e & 1) ? pair_halves<1>(x32[(e >> 1) + 20], x32[e >> 1])
+                                        : pair_halves<0>(x32[(e >> 1) + 20], x32[e >> 1]);
+                    }
+                    xa[wv][lane][2 * p + hh] = a;
+                }
+        }
+        __syncthreads();                          // the byte table is shared by the workgroup
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // (4) decode and contract, one MFMA per position (and half, 1.6-bit)
+    const float4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+    float4_t acc[NCLS];
+#pragma unroll
+    for (int c = 0; c < NCLS; ++c) acc[c] = zero4;
+#pragma unroll
+    for (int s = 0; s < CST; ++s) {
+        if (4 * (s * NW + wv) >= C) break;       // wave-uniform: no chunk of this step is live
+        const u32x4 *asrc = &xa[wv][4 * s + g][0];
+        u32x4 a[NOP];
+#pragma unroll
+        for (int p = 0; p < NOP; ++p) a[p] = asrc[p];
+        const u32x4 v = wq[s];
+        if constexpr (TWO) {
+            const u32x4 u = v >> 12u;
+#pragma unroll
+            for (int p = 0; p < 6; ++p) acc[p] = mfma(a[p], v & (0x00030003u << (2 * p)), acc[p]);
+            acc[0] = mfma(a[6], u & 0x00030003u, acc[0]);
+            acc[1] = mfma(a[7], u & 0x000C000Cu, acc[1]);
+        } else {
+            u32x4 lo, hi;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const uint32_t blo = (v[q >> 2] >> (8 * (q & 3))) & 0xFFu;
+                const uint32_t bhi = (v[2 + (q >> 2)] >> (8 * (q & 3))) & 0xFFu;
+                const uint32_t pq = lut[blo] | (lut[bhi] << 16);
+                if (q < 4) lo[q] = pq; else hi[q - 4] = pq;
+            }
+#pragma unroll
+            for (int p = 0; p < 5; ++p) {
+                const uint32_t m = 0x00030003u << (2 * p);
+                acc[p] = mfma(a[2 * p], lo & m, acc[p]);
+                acc[p] = mfma(a[2 * p + 1], hi & m, acc[p]);
+            }
+        }
+    }
+
+    // (5) merge classes (every row of a D tile is the same; row 0 is element 0 of lanes 0..15),
+    //     add the waves' partial sums in a fixed order, subtract sum_k x, scale, round
+    float xw[1] = {xsum};
+    const float xs_wave = wave_reduce_rows<1>(xw, lane);
+    float4_t t = acc[0] + 0.25f * acc[1];
+    t += 0.0625f * acc[2] + 0.015625f * acc[3];
+    t += 0.00390625f * acc[4];
+    if constexpr (TWO) t += 0.0009765625f * acc[5];
+    if (g == 0) red[wv][j] = t[0];
+    if (lane == 0) red[wv][16] = xs_wave;
+    __syncthreads();
+    if (threadIdx.x < 16 && n0 + (int)threadIdx.x < N) {
+        float sd = 0.f, sx = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            sd += red[w][threadIdx.x];
+            sx += red[w][16];
+        }
+        Y[n0 + threadIdx.x] = __builtin_bit_cast(uint16_t, (_Float16)((sd * 16777216.0f - sx) * scale));
+    }
+}
+
+template <int FMT, int NW, int CST>
+static void launch_cfg(const uint16_t *X, const uint8_t *Wp, float scale, int N, int K, int C, uint16_t *Y,
+                       hipStream_t s)
+{
+    hipLaunchKernelGGL((k_mv1<FMT, NW, CST>), dim3((N + 15) / 16), dim3(64 * NW), 0, s, X, Wp, scale, N, K, C, Y);
+}
+
+// Eight waves per 16 rows (measured best at K = 4096 and 11008); sixteen for long rows.
+template <int FMT>
+static bool launch_fmt(const uint16_t *X, const uint8_t *Wp, float scale, int N, int K, int C, uint16_t *Y,
+                       hipStream_t s)
+{
+    const int cst8 = (C + 31) / 32;              // chunk-steps with 8 waves (4 chunks per step and wave)
+    switch (cst8) {
+    case 1: launch_cfg<FMT, 8, 1>(X, Wp, scale, N, K, C, Y, s); return true;
+    case 2: launch_cfg<FMT, 8, 2>(X, Wp, scale, N, K, C, Y, s); return true;
+    case 3: launch_cfg<FMT, 8, 3>(X, Wp, scale, N, K, C, Y, s); return true;
+    case 4: launch_cfg<FMT, 8, 4>(X, Wp, scale, N, K, C, Y, s); return true;
+    case 5: launch_cfg<FMT, 8, 5>(X, Wp, scale, N, K, C, Y, s); return true;
+    case 6: launch_cfg<FMT, 8, 6>(X, Wp, scale, N, K, C, Y, s); return true;
+    case 7: launch_cfg<FMT, 8, 7>(X, Wp, scale, N, K, C, Y, s); return true;
+    case 8: launch_cfg<FMT, 8, 8>(X, Wp, scale, N, K, C, Y, s); return true;
+    default: break;
+    }
+    // sixteen waves; the staged activations of a workgroup must fit in LDS
+    const int cst16 = (C + 63) / 64;
+    if (cst16 <= 6) { launch_cfg<FMT, 16, 6>(X, Wp, scale, N, K, C, Y, s); return true; }
+    if constexpr (FMT == TRI_FMT_2BIT) {
+        if (cst16 <= 8) { launch_cfg<FMT, 16, 8>(X, Wp, scale, N, K, C, Y, s); return true; }
+        if (cst16 <= 12) { launch_cfg<FMT, 16, 12>(X, Wp, scale, N, K, C, Y, s); return true; }
+    }
+    return false;                                // longer rows: the streaming small-M kernel
+}
+
+bool launch_mv1(const uint16_t *X, const uint8_t *Wp, float scale, int N, int K, int fmt, uint16_t *Y, hipStream_t s)
+{
+    const int C = (int)(row_bytes(K, fmt) / 16);
+    // 32-bit buffer offsets: the activation row and one 16-row block stay below 2^31 bytes;
+    // activations are read in pieces of 8 values, so K must be a multiple of 8
+    if ((K % 8) != 0 || (int64_t)K * 2 >= ((int64_t)1 << 31) || 16 * (int64_t)C * 16 >= ((int64_t)1 << 31))
+        return false;
+    return fmt == TRI_FMT_2BIT ? launch_fmt<TRI_FMT_2BIT>(X, Wp, scale, N, K, C, Y, s)
+                               : launch_fmt<TRI_FMT_1P6BIT>(X, Wp, scale, N, K, C, Y, s);
+}
+
+}  // namespace tri

@@ -53,7 +53,8 @@ enum {
 enum {
     TRI_ALGO_AUTO = 0,     /* pick from (M, fmt): the default of tri_linear */
     TRI_ALGO_GEMV = 1,     /* M == 1, 2-bit only: VALU dot products, lanes own K-slices */
-    TRI_ALGO_SMALLM = 2,   /* 1 <= M <= 16: MFMA 16x16x32 f16 with trits decoded in registers */
+    TRI_ALGO_SMALLM = 2,   /* 1 <= M <= 16: MFMA 16x16x32 f16 with trits decoded in registers
+                              (also the choice at M = 1, where it outruns the VALU kernel) */
     TRI_ALGO_GEMM = 3      /* any M: tiled MFMA 32x32x16 f16 GEMM, activations staged in LDS and
                               trits decoded in registers (prefill) */
 };

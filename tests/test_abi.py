@@ -47,7 +47,7 @@ def test_status_strings():
 
 def test_select_algo():
     F2, F16 = tri.TRI_FMT_2BIT, tri.TRI_FMT_1P6BIT
-    assert tri.tri_select_algo(1, 4096, 4096, F2) == tri.TRI_ALGO_GEMV
+    assert tri.tri_select_algo(1, 4096, 4096, F2) == tri.TRI_ALGO_SMALLM   # the MFMA kernel also serves M = 1
     assert tri.tri_select_algo(1, 4096, 4096, F16) == tri.TRI_ALGO_SMALLM
     assert tri.tri_select_algo(16, 4096, 4096, F2) == tri.TRI_ALGO_SMALLM
     assert tri.tri_select_algo(17, 4096, 4096, F2) == tri.TRI_ALGO_GEMM
