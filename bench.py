@@ -16,7 +16,7 @@ of back-to-back launches of one kernel, queued while a sleep kernel holds the
 GPU, so no host time enters them (they agree with rocprofv3's per-dispatch
 durations).
 
-The same JSON line carries the roofline fraction of the GEMV kernel, the
+The same JSON line carries the roofline fraction of the decode kernel, the
 size-matched streaming-read floor, the CPU oracle timed on this host, and the
 batched-decode, block-step and prefill workloads.
 
@@ -37,7 +37,7 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E peak, GB/s
 MFMA_F16_PEAK_TFLOPS = 2516.6   # MI355X dense fp16 MFMA peak (256 CU x 4096 flop/clk x 2.4 GHz)
 METRIC = "effective HBM GB/s (% of peak) for M=1 ternary GEMV; prefill GEMM TFLOP/s (% MFMA)"
 COPIES = 64                     # distinct copies of every decode weight matrix
-COUNTERS = os.path.join(ROOT, "profiles", "decode_gemv_counters.md")
+COUNTERS = os.path.join(ROOT, "profiles", "decode_mv1_counters.md")
 
 
 def log(*a):
@@ -137,7 +137,7 @@ def read_floor(nbytes, clock, reps=200):
 
 
 def counters():
-    """HBM traffic of the GEMV kernel per decode step from the committed rocprofv3 summary,
+    """HBM traffic of the decode kernel per decode step from the committed rocprofv3 summary,
     or None when the kernel source changed after the counters were taken."""
     import hashlib
     if not os.path.exists(COUNTERS):
@@ -282,7 +282,7 @@ def main():
                    "M": 1, "shapes": [[K, N] for (_, K, N) in dcfg["shapes"]], "format": "2bit",
                    "accumulate": "f32", "bytes_per_step": step_bytes, "timing": "HIP graph replay"},
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
-        "roofline": {"bound": "hbm", "kernel": "k_gemv2 (tri_gemv.hip)", "achieved": round(achieved, 2),
+        "roofline": {"bound": "hbm", "kernel": "k_mv1 (tri_mv1.hip)", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": (ctr or {}).get("traffic_bytes_per_step"),
                      "algorithmic_bytes": step_bytes, "launches": len(per_launch),
