@@ -24,6 +24,9 @@ int launch_smallm(const uint16_t *X, const uint8_t *Wp, float scale, int M, int 
 // MFMA decode kernel with activations staged in LDS; false (nothing launched) if K is too long for it.
 // M = 1 on MFMA (tri_mv1.hip); false if the shape is outside its range
 bool launch_mv1(const uint16_t *X, const uint8_t *Wp, float scale, int N, int K, int fmt, uint16_t *Y, hipStream_t s);
+// 2 <= M <= 16 on MFMA (tri_mvm.hip); false if the shape is outside its range
+bool launch_mvm(const uint16_t *X, const uint8_t *Wp, float scale, int M, int N, int K, int fmt, uint16_t *Y,
+                hipStream_t s);
 bool launch_decode(const uint16_t *X, const uint8_t *Wp, float scale, int M, int N, int K, int fmt, uint16_t *Y,
                    hipStream_t s);
 int launch_gemm(const uint16_t *X, const uint8_t *Wp, float scale, int64_t M, int N, int K, int fmt, uint16_t *Y,
