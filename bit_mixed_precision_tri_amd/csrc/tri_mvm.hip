@@ -102,7 +102,7 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
     float4_t acc[NCLS];
 #pragma unroll
     for (int c = 0; c < NCLS; ++c) acc[c] = zero4;
-    float xsum = 0.f;                            // this lane's share of sum_k X[j][k]
+    float4_t accx = zero4;                       // sum_k X[m][k] in every column of the tile
     // the activations of PD steps are in flight at once (a ring of register sets; one step
     // ahead measured best: deeper rings gained nothing)
     constexpr int PD = 1;
@@ -125,8 +125,6 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
             x32[4 * q] = v[0]; x32[4 * q + 1] = v[1]; x32[4 * q + 2] = v[2]; x32[4 * q + 3] = v[3];
         }
         wave_sync();                             // the slot may be refilled at the next step
-#pragma unroll
-        for (int q = 0; q < XH / 2; ++q) xsum = dot2(x32[q], 0x3C003C00u, xsum);   // (x_lo, x_hi) . (1, 1)
         u32x4 a[NOP];
         if constexpr (TWO) {
 #pragma unroll
@@ -147,6 +145,10 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
                                                     : pair_halves<0>(x32[(e >> 1) + 20], x32[e >> 1]);
                     }
         }
+        // sum_k X[m][k] on the matrix cores: every A operand against a B of ones
+        const u32x4 ones = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
+#pragma unroll
+        for (int p = 0; p < NOP; ++p) accx = mfma(a[p], ones, accx);
         // decode and contract
         const u32x4 v = wq[s];
         if constexpr (TWO) {
@@ -173,22 +175,17 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
         }
     }
 
-    // merge classes: lane (g, j) holds rows 4g + e of column j; sum_k X[j][k] lives in the
-    // four lanes j, j+16, j+32, j+48 (one per chunk of a step)
+    // merge classes: lane (g, j) holds rows 4g + e of column j (of D and of the sums of X)
     float4_t t = acc[0] + 0.25f * acc[1];
     t += 0.0625f * acc[2] + 0.015625f * acc[3];
     t += 0.00390625f * acc[4];
     if constexpr (TWO) t += 0.0009765625f * acc[5];
 #pragma unroll
     for (int e = 0; e < 4; ++e) red[wv][4 * g + e][j] = t[e];
-    float xa = xsum, xb = xsum;
-    swap32(xa, xb);                              // lanes l and l^32 trade
-    xsum = xa + xb;
-    xa = xsum;
-    xb = xsum;
-    swap16(xa, xb);                              // lanes l and l^16 trade
-    xsum = xa + xb;
-    if (g == 0) red[wv][j][16] = xsum;
+    if (j == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red[wv][4 * g + e][16] = accx[e];
+    }
     __syncthreads();
     // thread (m, jj): output Y[m][n0 + jj], waves added in a fixed order
     for (int o = threadIdx.x; o < MT * 16; o += 64 * NW) {
