@@ -317,20 +317,63 @@ def bench_batched(clock):
 
 
 def bench_block(clock):
-    """The seven linears of one block decode step, back to back (inputs pre-staged)."""
+    """One block decode step: Q, K, V, O (4096x4096), gate, up (4096->11008), down (11008->4096),
+    inputs pre-staged, weights rotating over copies.  Timed as seven launches and as four,
+    with Q/K/V and gate/up each as one grouped launch (they read the same activations)."""
     import torch
-    from bit_mixed_precision_tri_amd import configs
+    import bit_mixed_precision_tri_amd as tri
+    from bit_mixed_precision_tri_amd import configs, synth
     cfg = configs.BLOCK
     res = []
+    copies = 16
     for M in cfg["Ms"]:
-        layers = [Layer(cfg["workload_id"], 100 * M + li, M, N, K, cfg["fmt"], copies=16)
-                  for li, (name, K, N) in enumerate(cfg["layers"])]
-        t, _ = clock.run([L.launch for _ in range(50) for L in layers])
-        tstep = t * len(layers)
-        nbytes = sum(L.bytes for L in layers)
-        res.append({"M": M, "launches": len(layers), "bytes": nbytes, "step_us": round(tstep * 1e6, 3),
-                    "GBps": round(nbytes / tstep / 1e9, 1), "frac_hbm": round(nbytes / tstep / 1e9 / HBM_PEAK_GBS, 4)})
-        del layers
+        pools, scales, Ns, Ks = [], [], [], []
+        for li, (name, K, N) in enumerate(cfg["layers"]):
+            W, _, s = synth.layer_inputs(cfg["workload_id"], 100 * M + li, M, N, K)
+            Wp = tri.pack(torch.from_numpy(W).cuda(), cfg["fmt"])
+            pool = torch.empty((copies,) + tuple(Wp.shape), dtype=torch.uint8, device="cuda")
+            pool[:] = Wp
+            pools.append(pool)
+            scales.append(s)
+            Ns.append(N)
+            Ks.append(K)
+        _, Xh, _ = synth.layer_inputs(cfg["workload_id"], 100 * M + 50, M, 1, cfg["hidden"])
+        _, Xm, _ = synth.layer_inputs(cfg["workload_id"], 100 * M + 51, M, 1, cfg["mlp"])
+        Xh, Xm = torch.from_numpy(Xh).cuda(), torch.from_numpy(Xm).cuda()
+        Ys = [torch.empty((M, N), dtype=torch.float16, device="cuda") for N in Ns]
+        nbytes = sum(effective_bytes(M, N, K, cfg["fmt"]) for N, K in zip(Ns, Ks))
+        F = cfg["fmt"]
+        ctr = [0]
+
+        def one(i, Xi):
+            c = ctr[0] % copies
+            tri.tri_linear(Xi, pools[i][c], scales[i], M, Ns[i], Ks[i], F, Ys[i])
+
+        def step7():
+            for i in range(7):
+                one(i, Xm if i == 6 else Xh)
+            ctr[0] += 1
+
+        def group(ids, Xi):
+            c = ctr[0] % copies
+            tri.tri_linear_grouped(Xi, [pools[i][c] for i in ids], [scales[i] for i in ids], M, [Ns[i] for i in ids],
+                                   Ks[ids[0]], F, [Ys[i] for i in ids])
+
+        def step4():
+            group([0, 1, 2], Xh)
+            one(3, Xh)
+            group([4, 5], Xh)
+            one(6, Xm)
+            ctr[0] += 1
+
+        t7, _ = clock.run([step7] * 50)
+        t4, _ = clock.run([step4] * 50)
+        res.append({"M": M, "bytes": nbytes,
+                    "separate": {"launches": 7, "step_us": round(t7 * 1e6, 3), "GBps": round(nbytes / t7 / 1e9, 1),
+                                 "frac_hbm": round(nbytes / t7 / 1e9 / HBM_PEAK_GBS, 4)},
+                    "grouped": {"launches": 4, "step_us": round(t4 * 1e6, 3), "GBps": round(nbytes / t4 / 1e9, 1),
+                                "frac_hbm": round(nbytes / t4 / 1e9 / HBM_PEAK_GBS, 4)}})
+        del pools
         torch.cuda.empty_cache()
     return res
 

@@ -47,6 +47,8 @@ def lib():
         L.tri_linear.restype = i32
         L.tri_linear_algo.argtypes = [p, p, ctypes.c_float, i64, i64, i64, i32, p, i32, p]
         L.tri_linear_algo.restype = i32
+        L.tri_linear_grouped.argtypes = [p, p, p, i64, p, i64, i32, p, i32, p]
+        L.tri_linear_grouped.restype = i32
         L.tri_select_algo.argtypes = [i64, i64, i64, i32]
         L.tri_select_algo.restype = i32
         L.tri_status_string.argtypes = [i32]
@@ -106,6 +108,22 @@ def tri_linear(X, Wp, scale, M, N, K, fmt, Y, stream=None):
 def tri_linear_algo(X, Wp, scale, M, N, K, fmt, Y, algo, stream=None):
     return _check(lib().tri_linear_algo(_ptr(X), _ptr(Wp), float(scale), int(M), int(N), int(K), int(fmt), _ptr(Y),
                                         int(algo), _stream(stream)), "tri_linear_algo")
+
+
+TRI_MAX_GROUPS = 4
+
+
+def tri_linear_grouped(X, Wps, scales, M, Ns, K, fmt, Ys, stream=None):
+    """Wps, scales, Ns, Ys: sequences of G entries (device tensors / floats / ints)."""
+    G = len(Wps)
+    if not (len(scales) == len(Ns) == len(Ys) == G):
+        raise ValueError("tri_linear_grouped: Wps, scales, Ns and Ys must have the same length")
+    wp = (ctypes.c_void_p * max(G, 1))(*[_ptr(w).value for w in Wps])
+    sc = (ctypes.c_float * max(G, 1))(*[float(v) for v in scales])
+    nn = (ctypes.c_int64 * max(G, 1))(*[int(v) for v in Ns])
+    yy = (ctypes.c_void_p * max(G, 1))(*[_ptr(y).value for y in Ys])
+    return _check(lib().tri_linear_grouped(_ptr(X), wp, sc, int(M), nn, int(K), int(fmt), yy, int(G),
+                                           _stream(stream)), "tri_linear_grouped")
 
 
 def tri_select_algo(M, N, K, fmt):

@@ -3,6 +3,7 @@
 #include "tri_internal.h"
 
 using namespace tri;
+static_assert(TRI_MAX_GROUPS == kMaxGroups, "group table size");
 
 namespace {
 
@@ -97,6 +98,37 @@ int tri_linear_algo(const _Float16 *X, const uint8_t *Wp, float scale, int64_t M
     if (rc != TRI_OK) return rc;
     if (algo == TRI_ALGO_AUTO) algo = select_algo(M, fmt);
     return run_linear(X, Wp, scale, M, N, K, fmt, Y, algo, stream);
+}
+
+int tri_linear_grouped(const _Float16 *X, const uint8_t *const *Wp, const float *scale, int64_t M, const int64_t *N,
+                       int64_t K, int fmt, _Float16 *const *Y, int G, hipStream_t stream)
+{
+    if (!Wp || !scale || !N || !Y || G < 1 || G > TRI_MAX_GROUPS) return TRI_EINVAL;
+    for (int g = 0; g < G; ++g) {
+        const int rc = check_linear(X, Wp[g], M, N[g], K, fmt, Y[g]);
+        if (rc != TRI_OK) return rc;
+    }
+    int64_t blocks = 0;
+    for (int g = 0; g < G; ++g) blocks += (N[g] + 15) / 16;
+    if (blocks >= ((int64_t)1 << 31)) return TRI_EINVAL;
+    const uint16_t *x = reinterpret_cast<const uint16_t *>(X);
+    if (M <= 16) {
+        int n[kMaxGroups];
+        uint16_t *y[kMaxGroups];
+        for (int g = 0; g < G; ++g) {
+            n[g] = (int)N[g];
+            y[g] = reinterpret_cast<uint16_t *>(Y[g]);
+        }
+        const Groups gr = make_groups(G, Wp, scale, n, y);
+        const bool done = M == 1 ? launch_mv1(x, gr, (int)K, fmt, stream) : launch_mvm(x, gr, (int)M, (int)K, fmt, stream);
+        if (done) return hipGetLastError() == hipSuccess ? TRI_OK : TRI_EHIP;
+    }
+    // shapes outside the grouped kernels' range (and M > 16): one launch per matrix
+    for (int g = 0; g < G; ++g) {
+        const int rc = run_linear(X, Wp[g], scale[g], M, N[g], K, fmt, Y[g], select_algo(M, fmt), stream);
+        if (rc != TRI_OK) return rc;
+    }
+    return TRI_OK;
 }
 
 const char *tri_status_string(int code)

@@ -258,8 +258,9 @@ bool launch_decode(const uint16_t *X, const uint8_t *Wp, float scale, int M, int
     // the activation pieces are 8 values wide, so K must be a multiple of 8
     if ((K % 8) != 0 || (int64_t)M * K * 2 >= ((int64_t)1 << 31) || 15 * (int64_t)C * 16 >= ((int64_t)1 << 31))
         return false;
-    if (M == 1) return launch_mv1(X, Wp, scale, N, K, fmt, Y, s);
-    if (launch_mvm(X, Wp, scale, M, N, K, fmt, Y, s)) return true;
+    const Groups gr = make_groups(1, &Wp, &scale, &N, &Y);
+    if (M == 1) return launch_mv1(X, gr, K, fmt, s);
+    if (launch_mvm(X, gr, M, K, fmt, s)) return true;
     return fmt == TRI_FMT_2BIT ? launch_mn<TRI_FMT_2BIT>(X, Wp, scale, M, N, K, C, Y, s)
                                : launch_mn<TRI_FMT_1P6BIT>(X, Wp, scale, M, N, K, C, Y, s);
 }

@@ -17,16 +17,55 @@ inline int64_t row_bytes(int64_t K, int fmt)
 int launch_pack(const int8_t *W, int64_t N, int64_t K, int fmt, uint8_t *Wp, hipStream_t s);
 int launch_unpack(const uint8_t *Wp, int64_t N, int64_t K, int fmt, int8_t *W, hipStream_t s);
 
+// Weight matrices that read the same activations, served by one launch (a grouped layer):
+// matrix g has N[g] rows and owns the 16-row blocks blk[g] .. blk[g+1]-1 of the grid.  A
+// single layer is the case G = 1.
+constexpr int kMaxGroups = 4;
+struct Groups {
+    const uint8_t *Wp[kMaxGroups];
+    uint16_t *Y[kMaxGroups];
+    float scale[kMaxGroups];
+    int N[kMaxGroups];
+    int blk[kMaxGroups + 1];
+    int G;
+};
+
+inline Groups make_groups(int G, const uint8_t *const *Wp, const float *scale, const int *N, uint16_t *const *Y)
+{
+    Groups gr{};
+    gr.G = G;
+    gr.blk[0] = 0;
+    for (int g = 0; g < G; ++g) {
+        gr.Wp[g] = Wp[g];
+        gr.Y[g] = Y[g];
+        gr.scale[g] = scale[g];
+        gr.N[g] = N[g];
+        gr.blk[g + 1] = gr.blk[g] + (N[g] + 15) / 16;
+    }
+    for (int g = G; g < kMaxGroups; ++g) gr.blk[g + 1] = gr.blk[G];
+    return gr;
+}
+
+// The matrix of a grouped launch that a workgroup (by its 16-row block) belongs to.
+__device__ __forceinline__ int group_of(const Groups &gr, int block)
+{
+    int gi = 0;
+#pragma unroll
+    for (int q = 1; q < kMaxGroups; ++q)
+        if (q < gr.G && block >= gr.blk[q]) gi = q;
+    return gi;
+}
+
 // Kernel launchers of the layer; arguments are already validated.
 int launch_gemv2(const uint16_t *X, const uint8_t *Wp, float scale, int N, int K, uint16_t *Y, hipStream_t s);
 int launch_smallm(const uint16_t *X, const uint8_t *Wp, float scale, int M, int N, int K, int fmt, uint16_t *Y,
                   hipStream_t s);
-// MFMA decode kernel with activations staged in LDS; false (nothing launched) if K is too long for it.
-// M = 1 on MFMA (tri_mv1.hip); false if the shape is outside its range
-bool launch_mv1(const uint16_t *X, const uint8_t *Wp, float scale, int N, int K, int fmt, uint16_t *Y, hipStream_t s);
-// 2 <= M <= 16 on MFMA (tri_mvm.hip); false if the shape is outside its range
-bool launch_mvm(const uint16_t *X, const uint8_t *Wp, float scale, int M, int N, int K, int fmt, uint16_t *Y,
-                hipStream_t s);
+// M = 1 on MFMA (tri_mv1.hip) and 2 <= M <= 16 on MFMA (tri_mvm.hip), for one or several
+// matrices; false (nothing launched) if the shape is outside their range.
+bool launch_mv1(const uint16_t *X, const Groups &gr, int K, int fmt, hipStream_t s);
+bool launch_mvm(const uint16_t *X, const Groups &gr, int M, int K, int fmt, hipStream_t s);
+// The small-M kernels for one matrix: the two above, else the LDS-staged kernel for short rows;
+// false (nothing launched) if none of them takes the shape.
 bool launch_decode(const uint16_t *X, const uint8_t *Wp, float scale, int M, int N, int K, int fmt, uint16_t *Y,
                    hipStream_t s);
 int launch_gemm(const uint16_t *X, const uint8_t *Wp, float scale, int64_t M, int N, int K, int fmt, uint16_t *Y,

@@ -53,9 +53,13 @@ __device__ __forceinline__ float4_t mfma(const u32x4 a, const u32x4 b, float4_t 
 }  // namespace
 
 template <int FMT, int NW, int CST>
-__global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X, const uint8_t *__restrict__ Wp,
-                                                 float scale, int N, int K, int C, uint16_t *__restrict__ Y)
+__global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X, const Groups gr, int K, int C)
 {
+    const int gi = group_of(gr, (int)blockIdx.x);
+    const uint8_t *__restrict__ Wp = gr.Wp[gi];
+    uint16_t *__restrict__ Y = gr.Y[gi];
+    const float scale = gr.scale[gi];
+    const int N = gr.N[gi];
     constexpr bool TWO = FMT == TRI_FMT_2BIT;
     constexpr int XH = TWO ? 64 : 80;            // activations per chunk
     constexpr int NOP = TWO ? 8 : 10;            // A operands (MFMAs) per chunk
@@ -73,7 +77,7 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar descriptors)
     const int g = lane >> 4;
     const int j = lane & 15;
-    const int n0 = blockIdx.x * 16;
+    const int n0 = ((int)blockIdx.x - gr.blk[gi]) * 16;
     const int64_t S = (int64_t)C * 16;
 
     if constexpr (!TWO) {
@@ -227,48 +231,45 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
 }
 
 template <int FMT, int NW, int CST>
-static void launch_cfg(const uint16_t *X, const uint8_t *Wp, float scale, int N, int K, int C, uint16_t *Y,
-                       hipStream_t s)
+static void launch_cfg(const uint16_t *X, const Groups &gr, int K, int C, hipStream_t s)
 {
-    hipLaunchKernelGGL((k_mv1<FMT, NW, CST>), dim3((N + 15) / 16), dim3(64 * NW), 0, s, X, Wp, scale, N, K, C, Y);
+    hipLaunchKernelGGL((k_mv1<FMT, NW, CST>), dim3(gr.blk[gr.G]), dim3(64 * NW), 0, s, X, gr, K, C);
 }
 
 // Eight waves per 16 rows (measured best at K = 4096 and 11008); sixteen for long rows.
 template <int FMT>
-static bool launch_fmt(const uint16_t *X, const uint8_t *Wp, float scale, int N, int K, int C, uint16_t *Y,
-                       hipStream_t s)
+static bool launch_fmt(const uint16_t *X, const Groups &gr, int K, int C, hipStream_t s)
 {
     const int cst8 = (C + 31) / 32;              // chunk-steps with 8 waves (4 chunks per step and wave)
     switch (cst8) {
-    case 1: launch_cfg<FMT, 8, 1>(X, Wp, scale, N, K, C, Y, s); return true;
-    case 2: launch_cfg<FMT, 8, 2>(X, Wp, scale, N, K, C, Y, s); return true;
-    case 3: launch_cfg<FMT, 8, 3>(X, Wp, scale, N, K, C, Y, s); return true;
-    case 4: launch_cfg<FMT, 8, 4>(X, Wp, scale, N, K, C, Y, s); return true;
-    case 5: launch_cfg<FMT, 8, 5>(X, Wp, scale, N, K, C, Y, s); return true;
-    case 6: launch_cfg<FMT, 8, 6>(X, Wp, scale, N, K, C, Y, s); return true;
-    case 7: launch_cfg<FMT, 8, 7>(X, Wp, scale, N, K, C, Y, s); return true;
-    case 8: launch_cfg<FMT, 8, 8>(X, Wp, scale, N, K, C, Y, s); return true;
+    case 1: launch_cfg<FMT, 8, 1>(X, gr, K, C, s); return true;
+    case 2: launch_cfg<FMT, 8, 2>(X, gr, K, C, s); return true;
+    case 3: launch_cfg<FMT, 8, 3>(X, gr, K, C, s); return true;
+    case 4: launch_cfg<FMT, 8, 4>(X, gr, K, C, s); return true;
+    case 5: launch_cfg<FMT, 8, 5>(X, gr, K, C, s); return true;
+    case 6: launch_cfg<FMT, 8, 6>(X, gr, K, C, s); return true;
+    case 7: launch_cfg<FMT, 8, 7>(X, gr, K, C, s); return true;
+    case 8: launch_cfg<FMT, 8, 8>(X, gr, K, C, s); return true;
     default: break;
     }
     // sixteen waves; the staged activations of a workgroup must fit in LDS
     const int cst16 = (C + 63) / 64;
-    if (cst16 <= 6) { launch_cfg<FMT, 16, 6>(X, Wp, scale, N, K, C, Y, s); return true; }
+    if (cst16 <= 6) { launch_cfg<FMT, 16, 6>(X, gr, K, C, s); return true; }
     if constexpr (FMT == TRI_FMT_2BIT) {
-        if (cst16 <= 8) { launch_cfg<FMT, 16, 8>(X, Wp, scale, N, K, C, Y, s); return true; }
-        if (cst16 <= 12) { launch_cfg<FMT, 16, 12>(X, Wp, scale, N, K, C, Y, s); return true; }
+        if (cst16 <= 8) { launch_cfg<FMT, 16, 8>(X, gr, K, C, s); return true; }
+        if (cst16 <= 12) { launch_cfg<FMT, 16, 12>(X, gr, K, C, s); return true; }
     }
     return false;                                // longer rows: the streaming small-M kernel
 }
 
-bool launch_mv1(const uint16_t *X, const uint8_t *Wp, float scale, int N, int K, int fmt, uint16_t *Y, hipStream_t s)
+bool launch_mv1(const uint16_t *X, const Groups &gr, int K, int fmt, hipStream_t s)
 {
     const int C = (int)(row_bytes(K, fmt) / 16);
     // 32-bit buffer offsets: the activation row and one 16-row block stay below 2^31 bytes;
     // activations are read in pieces of 8 values, so K must be a multiple of 8
     if ((K % 8) != 0 || (int64_t)K * 2 >= ((int64_t)1 << 31) || 16 * (int64_t)C * 16 >= ((int64_t)1 << 31))
         return false;
-    return fmt == TRI_FMT_2BIT ? launch_fmt<TRI_FMT_2BIT>(X, Wp, scale, N, K, C, Y, s)
-                               : launch_fmt<TRI_FMT_1P6BIT>(X, Wp, scale, N, K, C, Y, s);
+    return fmt == TRI_FMT_2BIT ? launch_fmt<TRI_FMT_2BIT>(X, gr, K, C, s) : launch_fmt<TRI_FMT_1P6BIT>(X, gr, K, C, s);
 }
 
 }  // namespace tri

@@ -47,9 +47,13 @@ __device__ __forceinline__ void wave_sync()
 }  // namespace
 
 template <int FMT, int MT, int NW, int CST>
-__global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X, const uint8_t *__restrict__ Wp,
-                                                 float scale, int M, int N, int K, int C, uint16_t *__restrict__ Y)
+__global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X, const Groups gr, int M, int K, int C)
 {
+    const int gi = group_of(gr, (int)blockIdx.x);
+    const uint8_t *__restrict__ Wp = gr.Wp[gi];
+    uint16_t *__restrict__ Y = gr.Y[gi];
+    const float scale = gr.scale[gi];
+    const int N = gr.N[gi];
     constexpr bool TWO = FMT == TRI_FMT_2BIT;
     constexpr int XH = TWO ? 64 : 80;            // activations per chunk
     constexpr int NOP = TWO ? 8 : 10;            // A operands (MFMAs) per chunk
@@ -65,7 +69,7 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar descriptors)
     const int g = lane >> 4;
     const int j = lane & 15;
-    const int n0 = blockIdx.x * 16;
+    const int n0 = ((int)blockIdx.x - gr.blk[gi]) * 16;
     const int64_t S = (int64_t)C * 16;
 
     if constexpr (!TWO) {
@@ -203,39 +207,36 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
 }
 
 template <int FMT, int MT, int NW, int CST>
-static void launch_cfg(const uint16_t *X, const uint8_t *Wp, float scale, int M, int N, int K, int C, uint16_t *Y,
-                       hipStream_t s)
+static void launch_cfg(const uint16_t *X, const Groups &gr, int M, int K, int C, hipStream_t s)
 {
-    hipLaunchKernelGGL((k_mvm<FMT, MT, NW, CST>), dim3((N + 15) / 16), dim3(64 * NW), 0, s, X, Wp, scale, M, N, K, C, Y);
+    hipLaunchKernelGGL((k_mvm<FMT, MT, NW, CST>), dim3(gr.blk[gr.G]), dim3(64 * NW), 0, s, X, gr, M, K, C);
 }
 
 template <int FMT, int MT>
-static bool launch_mt(const uint16_t *X, const uint8_t *Wp, float scale, int M, int N, int K, int C, uint16_t *Y,
-                      hipStream_t s)
+static bool launch_mt(const uint16_t *X, const Groups &gr, int M, int K, int C, hipStream_t s)
 {
     const int cst8 = (C + 31) / 32;              // chunk-steps with 8 waves (4 chunks per step and wave)
     switch (cst8) {
-    case 1: launch_cfg<FMT, MT, 8, 1>(X, Wp, scale, M, N, K, C, Y, s); return true;
-    case 2: launch_cfg<FMT, MT, 8, 2>(X, Wp, scale, M, N, K, C, Y, s); return true;
-    case 3: launch_cfg<FMT, MT, 8, 3>(X, Wp, scale, M, N, K, C, Y, s); return true;
-    case 4: launch_cfg<FMT, MT, 8, 4>(X, Wp, scale, M, N, K, C, Y, s); return true;
-    case 5: launch_cfg<FMT, MT, 8, 5>(X, Wp, scale, M, N, K, C, Y, s); return true;
-    case 6: launch_cfg<FMT, MT, 8, 6>(X, Wp, scale, M, N, K, C, Y, s); return true;
-    case 7: launch_cfg<FMT, MT, 8, 7>(X, Wp, scale, M, N, K, C, Y, s); return true;
-    case 8: launch_cfg<FMT, MT, 8, 8>(X, Wp, scale, M, N, K, C, Y, s); return true;
+    case 1: launch_cfg<FMT, MT, 8, 1>(X, gr, M, K, C, s); return true;
+    case 2: launch_cfg<FMT, MT, 8, 2>(X, gr, M, K, C, s); return true;
+    case 3: launch_cfg<FMT, MT, 8, 3>(X, gr, M, K, C, s); return true;
+    case 4: launch_cfg<FMT, MT, 8, 4>(X, gr, M, K, C, s); return true;
+    case 5: launch_cfg<FMT, MT, 8, 5>(X, gr, M, K, C, s); return true;
+    case 6: launch_cfg<FMT, MT, 8, 6>(X, gr, M, K, C, s); return true;
+    case 7: launch_cfg<FMT, MT, 8, 7>(X, gr, M, K, C, s); return true;
+    case 8: launch_cfg<FMT, MT, 8, 8>(X, gr, M, K, C, s); return true;
     default: break;
     }
     // sixteen waves, while the per-wave activation slots fit in LDS
     if constexpr (FMT == TRI_FMT_2BIT || MT <= 8) {
         const int cst16 = (C + 63) / 64;
-        if (cst16 <= 8) { launch_cfg<FMT, MT, 16, 8>(X, Wp, scale, M, N, K, C, Y, s); return true; }
-        if (cst16 <= 16) { launch_cfg<FMT, MT, 16, 16>(X, Wp, scale, M, N, K, C, Y, s); return true; }
+        if (cst16 <= 8) { launch_cfg<FMT, MT, 16, 8>(X, gr, M, K, C, s); return true; }
+        if (cst16 <= 16) { launch_cfg<FMT, MT, 16, 16>(X, gr, M, K, C, s); return true; }
     }
     return false;                                // longer rows: the streaming small-M kernel
 }
 
-bool launch_mvm(const uint16_t *X, const uint8_t *Wp, float scale, int M, int N, int K, int fmt, uint16_t *Y,
-                hipStream_t s)
+bool launch_mvm(const uint16_t *X, const Groups &gr, int M, int K, int fmt, hipStream_t s)
 {
     const int C = (int)(row_bytes(K, fmt) / 16);
     // 32-bit buffer offsets: the activations and one 16-row block stay below 2^31 bytes;
@@ -243,14 +244,10 @@ bool launch_mvm(const uint16_t *X, const uint8_t *Wp, float scale, int M, int N,
     if (M < 2 || M > 16 || (K % 8) != 0 || (int64_t)M * K * 2 >= ((int64_t)1 << 31) ||
         16 * (int64_t)C * 16 >= ((int64_t)1 << 31))
         return false;
-    if (M <= 4)
-        return fmt == TRI_FMT_2BIT ? launch_mt<TRI_FMT_2BIT, 4>(X, Wp, scale, M, N, K, C, Y, s)
-                                   : launch_mt<TRI_FMT_1P6BIT, 4>(X, Wp, scale, M, N, K, C, Y, s);
-    if (M <= 8)
-        return fmt == TRI_FMT_2BIT ? launch_mt<TRI_FMT_2BIT, 8>(X, Wp, scale, M, N, K, C, Y, s)
-                                   : launch_mt<TRI_FMT_1P6BIT, 8>(X, Wp, scale, M, N, K, C, Y, s);
-    return fmt == TRI_FMT_2BIT ? launch_mt<TRI_FMT_2BIT, 16>(X, Wp, scale, M, N, K, C, Y, s)
-                               : launch_mt<TRI_FMT_1P6BIT, 16>(X, Wp, scale, M, N, K, C, Y, s);
+    const bool two = fmt == TRI_FMT_2BIT;
+    if (M <= 4) return two ? launch_mt<TRI_FMT_2BIT, 4>(X, gr, M, K, C, s) : launch_mt<TRI_FMT_1P6BIT, 4>(X, gr, M, K, C, s);
+    if (M <= 8) return two ? launch_mt<TRI_FMT_2BIT, 8>(X, gr, M, K, C, s) : launch_mt<TRI_FMT_1P6BIT, 8>(X, gr, M, K, C, s);
+    return two ? launch_mt<TRI_FMT_2BIT, 16>(X, gr, M, K, C, s) : launch_mt<TRI_FMT_1P6BIT, 16>(X, gr, M, K, C, s);
 }
 
 }  // namespace tri

@@ -103,6 +103,19 @@ int tri_linear_algo(const _Float16 *X, const uint8_t *Wp, float scale,
                     int64_t M, int64_t N, int64_t K, int fmt, _Float16 *Y,
                     int algo, hipStream_t stream);
 
+/* Several ternary linear layers that read the same activations, in one launch (for
+ * example the Q, K and V projections of a block, or its gate and up projections): for
+ * g < G,  Y[g] = fp16_rne(scale[g] * X W_g^T)  with W_g of N[g] rows packed for this K and
+ * fmt, exactly as tri_linear would compute each one.  Wp, scale, N and Y are HOST arrays of
+ * G entries (the pointers they hold are device pointers, with tri_linear's alignment and
+ * aliasing rules); 1 <= G <= TRI_MAX_GROUPS.  For M <= 16 one launch serves all G matrices
+ * (the launch's fixed cost is paid once); other shapes run one launch per matrix.
+ * Errors: those of tri_linear for any matrix, TRI_EINVAL for a bad G or a null array. */
+enum { TRI_MAX_GROUPS = 4 };
+int tri_linear_grouped(const _Float16 *X, const uint8_t *const *Wp, const float *scale, int64_t M,
+                       const int64_t *N, int64_t K, int fmt, _Float16 *const *Y, int G,
+                       hipStream_t stream);
+
 /* The algorithm tri_linear would pick for (M, N, K, fmt); TRI_EINVAL if invalid. */
 int tri_select_algo(int64_t M, int64_t N, int64_t K, int fmt);
 

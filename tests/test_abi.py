@@ -105,3 +105,24 @@ def test_probe_argument_errors_launch_nothing():
 def test_binding_raises_on_error_status():
     with pytest.raises(tri.TriError):
         tri.tri_linear(A, B, 1.0, 0, 4, 64, tri.TRI_FMT_2BIT, C, stream=0)
+
+
+def test_grouped_argument_errors_launch_nothing():
+    import ctypes
+    F2 = tri.TRI_FMT_2BIT
+    s = None
+    ptrs = lambda *v: (ctypes.c_void_p * len(v))(*v)
+    floats = lambda *v: (ctypes.c_float * len(v))(*v)
+    ints = lambda *v: (ctypes.c_int64 * len(v))(*v)
+    wp, sc, nn, yy = ptrs(B, B), floats(1.0, 1.0), ints(4, 8), ptrs(C, C)
+    for G in (0, -1, tri.TRI_MAX_GROUPS + 1):
+        assert raw("tri_linear_grouped", A, wp, sc, 1, nn, 64, F2, yy, G, s) == tri.TRI_EINVAL
+    assert raw("tri_linear_grouped", A, None, sc, 1, nn, 64, F2, yy, 2, s) == tri.TRI_EINVAL
+    assert raw("tri_linear_grouped", A, wp, None, 1, nn, 64, F2, yy, 2, s) == tri.TRI_EINVAL
+    assert raw("tri_linear_grouped", A, wp, sc, 1, None, 64, F2, yy, 2, s) == tri.TRI_EINVAL
+    assert raw("tri_linear_grouped", A, wp, sc, 1, nn, 64, F2, None, 2, s) == tri.TRI_EINVAL
+    # any bad matrix rejects the whole call
+    assert raw("tri_linear_grouped", A, ptrs(B, ODD), sc, 1, nn, 64, F2, yy, 2, s) == tri.TRI_EALIGN
+    assert raw("tri_linear_grouped", A, wp, sc, 1, ints(4, 0), 64, F2, yy, 2, s) == tri.TRI_EINVAL
+    assert raw("tri_linear_grouped", A, wp, sc, 1, nn, 64, F2, ptrs(C, None), 2, s) == tri.TRI_EINVAL
+    assert raw("tri_linear_grouped", None, wp, sc, 1, nn, 64, F2, yy, 2, s) == tri.TRI_EINVAL

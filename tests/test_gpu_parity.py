@@ -297,3 +297,29 @@ def test_gemm_full_tiles_ragged_edges(fmt):
     assert np.all(np.isfinite(Y))
     worst, exact = check_layer(Y, X, W, s, "gemm edges fmt=%d" % fmt, rows=GEMM_EDGE_ROWS)
     say("  worst err/tol %.3g, fraction equal to fp16(ref) %.3f" % (worst, exact))
+
+
+# Grouped layers: several matrices reading the same activations, one launch for M <= 16
+# (K = 1000: the grouped kernels; K = 1001: one launch per matrix).
+GROUPED = [(1, 1000), (3, 1000), (16, 1000), (1, 1001), (5, 1001), (20, 1000)]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("case", GROUPED, ids=["M%dK%d" % c for c in GROUPED])
+def test_grouped_layers(fmt, case):
+    import torch
+    M, K = case
+    Ns = [37, 256, 100]
+    X = synth.activations(synth.rng_for(400 + fmt, M, synth.STREAM_X), M, K)
+    Ws = [synth.trits(synth.rng_for(400 + fmt, 10 * M + g, synth.STREAM_W), n, K) for g, n in enumerate(Ns)]
+    scales = [0.02, -0.03, 0.045]
+    Xd = cuda(X)
+    Wps = [tri.pack(cuda(W), fmt) for W in Ws]
+    Ys = [torch.empty((M, n), dtype=torch.float16, device="cuda") for n in Ns]
+    say("grouped M=%d K=%d fmt=%d" % (M, K, fmt))
+    tri.tri_linear_grouped(Xd, Wps, scales, M, Ns, K, fmt, Ys)
+    for g, (W, s, Y) in enumerate(zip(Ws, scales, Ys)):
+        Yh = host(Y)
+        check_layer(Yh, X, W, s, "grouped M=%d K=%d fmt=%d g=%d" % (M, K, fmt, g))
+        # the same kernels as a single layer: identical results
+        np.testing.assert_array_equal(Yh, host(tri.linear(Xd, Wps[g], s, K, fmt)))
