@@ -117,7 +117,11 @@ def test_special_values():
                     Y = run_layer(X, Wp, s, K, fmt, algo)
                     check_layer(Y, X, W, s, "special fmt=%d algo=%d" % (fmt, algo))
                     if not W.any():
-                        assert np.all(Y == 0)
+                        # K % 8 != 0: every kernel serving this shape subtracts the -1 offset as an
+                        # exact zero-trit sum, so zero weights give exact zeros.  (The M <= 16
+                        # MFMA kernels for K % 8 == 0 subtract sum_k x instead; there W = 0 is
+                        # held to the tolerance above.)
+                        assert K % 8 != 0 and np.all(Y == 0)
                     # a one-hot activation row returns fp16(scale * t[:, 123]) exactly
                     np.testing.assert_array_equal(Y[2], (np.float32(s) * W[:, 123]).astype(np.float16))
 
