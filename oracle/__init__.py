@@ -1,8 +1,9 @@
 """CPU oracle for the ternary linear layer -- TEST INFRASTRUCTURE ONLY.
 
 This package wraps ``tri_oracle.c``: a plain, slow, scalar C implementation of
-the 2-bit and 1.6-bit packings, their inverse, and the ternary linear layer
-``Y = scale * (X @ W.T)`` summed in float64.  It exists to check the HIP library,
+the 2-bit and 1.6-bit packings, their inverse, the ternary linear layer
+``Y = scale * (X @ W.T)`` summed in float64, and the quantiser from latent
+float32 weights to trits and a scale.  It exists to check the HIP library,
 and only the test suite, the smoke check and the CPU-baseline leg of the
 benchmark may import it.  It shares no code with the HIP library (the only
 common module is the seeded input generator, which holds none of the layer's
@@ -64,6 +65,8 @@ def _load():
         lib.oracle_half_to_double.restype = ctypes.c_double
         lib.oracle_linear_f64.argtypes = [p, p, ctypes.c_double, i64, i64, i64, p, ctypes.c_int]
         lib.oracle_linear_f64.restype = ctypes.c_int
+        lib.oracle_quantize.argtypes = [p, i64, i64, p, p]
+        lib.oracle_quantize.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -140,6 +143,18 @@ def linear_f64(X, W, scale, nthreads=0):
 def linear_packed_f64(X, Wp, K, fmt, scale, nthreads=0):
     """The layer evaluated from the packed weights: unpack, then linear_f64."""
     return linear_f64(X, unpack(Wp, K, fmt), scale, nthreads)
+
+
+def quantize(W):
+    """Latent float32 weights (N, K) -> (trits (N, K) int8, float32 scale): the scale is the
+    float64 mean of |w| rounded to float32, a trit is round-half-even(w / scale) clipped to [-1, 1]."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    N, K = W.shape
+    T = np.empty((N, K), dtype=np.int8)
+    s = np.zeros(1, dtype=np.float32)
+    if N and K and _load().oracle_quantize(_ptr(W), N, K, _ptr(T), _ptr(s)) != 0:
+        raise ValueError("non-finite weight")
+    return T, np.float32(s[0])
 
 
 def max_threads():

@@ -24,6 +24,10 @@
  *   [SP] "Spectra 1.1: Scaling Laws and Efficient Inference for Ternary Language
  *        Models" (shd-paper.top summary), abstract: 2-bit and 1.6-bit packing of
  *        ternary weights.
+ *   For the quantiser, [PR] "What carries the argument" (latent full-precision
+ *   weights rounded on the fly in the forward pass) and the review's list of
+ *   domain assumptions (round-to-nearest ternary quantisation, straight-through
+ *   estimation).
  *
  * Readings taken where the pages are silent (stated once here, used below):
  *   - digit of a trit t is d = t + 1 in {0,1,2} (non-negative base-4 / base-3 digits);
@@ -35,7 +39,11 @@
  *   - unpack is defined for every byte value: 2-bit code 3 gives 0; 1.6-bit bytes
  *     243..255 go through the same repeated division by 3;
  *   - the layer returns scale * sum_k t[n][k] * x[m][k] exactly as summed in
- *     float64 in k order, unrounded.
+ *     float64 in k order, unrounded;
+ *   - the quantiser's scale (the pages do not give its rule) is the mean absolute
+ *     value of the matrix, summed in float64 and rounded once to float32; a weight
+ *     becomes round-half-to-even(w / scale) clipped to [-1, 1], and a zero scale
+ *     gives zero trits.
  *
  * Build: gcc -O2 -fopenmp -shared -fPIC tri_oracle.c -o liboracle.so
  */
@@ -179,6 +187,40 @@ int oracle_linear_f64(const uint16_t *X, const int8_t *W, double scale,
                 sum += (double)W[n * K + k] * oracle_half_to_double(X[m * K + k]);
             Y[m * N + n] = scale * sum;
         }
+    }
+    return 0;
+}
+
+/* Ternary quantisation of latent full-precision weights ([PR] "What carries the
+ * argument": the layer's weights are latent full-precision values rounded on the
+ * fly to {-1,0,1} times one shared scale; the review's domain assumptions name the
+ * rounding as round-to-nearest).  The scale rule is a reading (see the header):
+ *   scale = (sum_n sum_k |w[n][k]|) / (N*K), each row summed in k order, the row
+ *           sums added in n order, all in float64, then rounded to float32;
+ *   t[n][k] = clip(round_half_even(w[n][k] / scale), -1, 1), or 0 when scale == 0.
+ * W is N*K float32 row-major; T receives N*K trits.  Returns 0, or -1 if W holds a
+ * non-finite value. */
+int oracle_quantize(const float *W, int64_t N, int64_t K, int8_t *T, float *scale)
+{
+    for (int64_t i = 0; i < N * K; ++i)
+        if (!isfinite(W[i])) return -1;
+    double total = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+        double row = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            row += fabs((double)W[n * K + k]);
+        total += row;
+    }
+    float s = (float)(total / ((double)N * (double)K));
+    *scale = s;
+    for (int64_t i = 0; i < N * K; ++i) {
+        double q = 0.0;
+        if (s != 0.0f) {
+            q = rint((double)W[i] / (double)s);    /* nearest, ties to even (default rounding mode) */
+            if (q > 1.0) q = 1.0;
+            if (q < -1.0) q = -1.0;
+        }
+        T[i] = (int8_t)q;
     }
     return 0;
 }

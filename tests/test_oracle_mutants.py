@@ -34,6 +34,12 @@ MUTANTS = [
     ("fp16 exponent bias", "exponent - 25", "exponent - 24"),
     ("fp16 subnormal scale", "ldexp((double)mantissa, -24)", "ldexp((double)mantissa, -25)"),
     ("fp16 sign dropped", "return sign ? -v : v;", "return v;"),
+    ("quantise without abs", "row += fabs((double)W[n * K + k]);", "row += (double)W[n * K + k];"),
+    ("quantise ties away from zero", "q = rint((double)W[i] / (double)s);", "q = round((double)W[i] / (double)s);"),
+    ("quantise not clipped", "if (q > 1.0) q = 1.0;", ";"),
+    ("quantise mean over K only", "(double)N * (double)K", "(double)K"),
+    ("quantise sign flipped", "T[i] = (int8_t)q;", "T[i] = (int8_t)-q;"),
+    ("quantise threshold at the scale", "q = rint((double)W[i] / (double)s);", "q = rint((double)W[i] / (double)s / 2.0);"),
 ]
 
 

@@ -254,3 +254,90 @@ def test_tolerance_formula_shape():
     Yref = np.array([[10.0, -4.0]])
     tol = oracle.tolerance(X, -0.5, Yref)
     np.testing.assert_allclose(tol, [[2e-3 * 0.5 * 3.5 + 1e-2, 2e-3 * 0.5 * 3.5 + 4e-3]])
+
+
+# ---------------------------------------------------------------- quantiser (latent weights -> trits + scale)
+# Pins: hand-worked ties and clipping, exact recovery of a scaled ternary matrix, the scale against
+# numpy's mean (a library routine summing in another order), power-of-two and sign invariance, the
+# degenerate cases, and the zero fraction of Gaussian weights against its closed form.
+
+def test_quantize_worked_ties_and_clipping():
+    # sum |w| = 4 over 4 weights, so the scale is exactly 1 and w / scale = w:
+    #   0.5 + 2^-20 -> 1 (above the midpoint);  0.5 -> 0 (a tie goes to the even neighbour 0);
+    #   -(0.5 - 2^-20) -> 0;  2.5 -> round 2, clipped to 1
+    T, s = oracle.quantize(np.array([[0.5 + 2.0 ** -20, 0.5, -(0.5 - 2.0 ** -20), 2.5]], np.float32))
+    assert s == np.float32(1.0)
+    np.testing.assert_array_equal(T, [[1, 0, 0, 1]])
+    #   -0.5 -> 0 (tie);  -1.5 -> -2 (tie to even), clipped to -1;  1 -> 1;  1 -> 1
+    T, s = oracle.quantize(np.array([[-0.5, -1.5, 1.0, 1.0]], np.float32))
+    assert s == np.float32(1.0)
+    np.testing.assert_array_equal(T, [[0, -1, 1, 1]])
+    # two rows: sum |w| = 0.75 + 0.25 + 0.5 + 0.5 = 2 over 4 weights, scale 0.5;
+    # w / scale = 1.5 -> 1 (clipped from 2), 0.5 -> 0 (tie), -1 -> -1, 1 -> 1
+    T, s = oracle.quantize(np.array([[0.75, 0.25], [-0.5, 0.5]], np.float32))
+    assert s == np.float32(0.5)
+    np.testing.assert_array_equal(T, [[1, 0], [-1, 1]])
+
+
+@pytest.mark.parametrize("c", [0.0123, 3.5, 1e-3, 7.0e-6])
+def test_quantize_recovers_scaled_ternary(c):
+    from fractions import Fraction
+    rng = synth.rng_for(950, 0, 0)
+    Tin = synth.trits(rng, 23, 157)
+    c32 = np.float32(c)
+    W = Tin.astype(np.float32) * c32                   # exact: entries are 0 and +-c32
+    T, s = oracle.quantize(W)
+    np.testing.assert_array_equal(T, Tin)            # |w| / scale = N*K / nnz >= 1 for nonzeros
+    exact = Fraction(float(c32)) * int(np.count_nonzero(Tin)) / Tin.size
+    assert abs(Fraction(float(s)) - exact) <= Fraction(float(np.spacing(s)))
+
+
+def test_quantize_scale_is_the_mean_absolute_value():
+    rng = synth.rng_for(951, 0, 0)
+    for (N, K, std) in [(37, 301, 0.02), (5, 4096, 1.0), (300, 7, 3e-4)]:
+        W = (rng.standard_normal((N, K)) * std).astype(np.float32)
+        _, s = oracle.quantize(W)
+        ref = np.float32(np.mean(np.abs(W.astype(np.float64))))
+        assert abs(float(s) - float(ref)) <= float(np.spacing(ref)), (N, K, s, ref)
+
+
+def test_quantize_power_of_two_and_sign_invariance():
+    rng = synth.rng_for(952, 0, 0)
+    W = (rng.standard_normal((19, 211)) * 0.05).astype(np.float32)
+    T, s = oracle.quantize(W)
+    for e in (-7, 5):
+        T2, s2 = oracle.quantize(W * np.float32(2.0 ** e))
+        np.testing.assert_array_equal(T2, T)
+        assert s2 == s * np.float32(2.0 ** e)
+    Tn, sn = oracle.quantize(-W)
+    np.testing.assert_array_equal(Tn, -T)
+    assert sn == s
+
+
+def test_quantize_degenerate_cases():
+    T, s = oracle.quantize(np.zeros((3, 5), np.float32))
+    assert s == 0 and not T.any()
+    T, s = oracle.quantize(np.array([[-3.0]], np.float32))
+    assert s == np.float32(3.0) and T[0, 0] == -1
+    # one subnormal among many zeros: the mean underflows to a zero scale, and a zero scale gives zero trits
+    W = np.zeros((64, 64), np.float32)
+    W[3, 4] = np.float32(1.4e-45)
+    T, s = oracle.quantize(W)
+    assert s == 0 and not T.any()
+    for bad in (np.inf, -np.inf, np.nan):
+        W = np.ones((2, 3), np.float32)
+        W[1, 2] = bad
+        with pytest.raises(ValueError):
+            oracle.quantize(W)
+
+
+def test_quantize_zero_fraction_of_gaussian_weights():
+    # For w ~ N(0, sigma^2) the scale tends to E|w| = sigma*sqrt(2/pi), and a weight rounds to 0 when
+    # |w| < scale/2, which has probability erf(sqrt(2/pi)/2/sqrt(2)) = erf(1/(2*sqrt(pi))) ~ 0.3103.
+    rng = synth.rng_for(953, 0, 0)
+    W = (rng.standard_normal((1000, 1000)) * 0.02).astype(np.float32)
+    T, s = oracle.quantize(W)
+    p0 = math.erf(0.5 / math.sqrt(math.pi))
+    assert abs(np.mean(T == 0) - p0) < 3e-3
+    assert abs(np.mean(T == 1) - (1 - p0) / 2) < 3e-3
+    assert abs(float(s) - 0.02 * math.sqrt(2.0 / math.pi)) < 1e-4
