@@ -294,6 +294,7 @@ def main():
         out["batched"] = bench_batched(clock)
         out["block"] = bench_block(clock)
         out["prefill"] = bench_prefill(clock)
+        out["quantize"] = bench_quantize(clock)
     if not args.skip_cpu:
         out["cpu_baseline"] = cpu_baseline(dcfg["shapes"])
     print(json.dumps(out), flush=True)
@@ -392,6 +393,32 @@ def bench_prefill(clock):
                         "TFLOPs": round(tf, 2), "frac_mfma": round(tf / MFMA_F16_PEAK_TFLOPS, 4)})
             del L
             torch.cuda.empty_cache()
+    return res
+
+
+def bench_quantize(clock):
+    """tri_quantize on the prefill matrices (235M latent float32 weights each): the weights are read
+    twice (mean |w|, then the trits), the packed bytes written once."""
+    import torch
+    import bit_mixed_precision_tri_amd as tri
+    from bit_mixed_precision_tri_amd import configs, synth
+    cfg = configs.PREFILL
+    res = []
+    for fmt in cfg["fmts"]:
+        K, N = cfg["shapes"][0][1], cfg["shapes"][0][2]
+        W = torch.from_numpy(synth.latent_weights(synth.rng_for(cfg["workload_id"], 90 + fmt, synth.STREAM_LATENT),
+                                                  N, K)).cuda()
+        Wp = torch.empty((N, tri.tri_row_bytes(K, fmt)), dtype=torch.uint8, device="cuda")
+        scale = torch.empty(1, dtype=torch.float32, device="cuda")
+        nws = tri.tri_quantize_workspace_bytes(N, K)
+        ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+        t, _ = clock.run([lambda: tri.tri_quantize(W, N, K, fmt, Wp, scale, ws, nws)] * 10, warmup=2)
+        nbytes = 2 * 4 * N * K + Wp.numel()
+        res.append({"shape": "%dx%d" % (N, K), "format": configs.FMT_NAMES[fmt], "us": round(t * 1e6, 1),
+                    "bytes": nbytes, "GBps": round(nbytes / t / 1e9, 1),
+                    "frac_hbm": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)})
+        del W, Wp, ws
+        torch.cuda.empty_cache()
     return res
 
 

@@ -5,7 +5,8 @@ they only marshal arguments (device pointers of torch tensors, the current HIP
 stream) and raise ``TriError`` on a negative status.  All the work runs in the
 library's HIP kernels; there is no fallback of any kind -- if ``libtri.so`` is
 missing, every call raises.  The helpers at the end (``pack``, ``unpack``,
-``linear``) allocate their outputs with torch and then call the same entry points.
+``quantize``, ``linear``) allocate their outputs with torch and then call the same
+entry points.
 """
 import ctypes
 import os
@@ -43,6 +44,10 @@ def lib():
             getattr(L, name).restype = i32
         L.tri_unpack.argtypes = [p, i64, i64, i32, p, p]
         L.tri_unpack.restype = i32
+        L.tri_quantize_workspace_bytes.argtypes = [i64, i64]
+        L.tri_quantize_workspace_bytes.restype = i64
+        L.tri_quantize.argtypes = [p, i64, i64, i32, p, p, p, i64, p]
+        L.tri_quantize.restype = i32
         L.tri_linear.argtypes = [p, p, ctypes.c_float, i64, i64, i64, i32, p, p]
         L.tri_linear.restype = i32
         L.tri_linear_algo.argtypes = [p, p, ctypes.c_float, i64, i64, i64, i32, p, i32, p]
@@ -98,6 +103,15 @@ def tri_pack16(W, N, K, Wp, stream=None):
 
 def tri_unpack(Wp, N, K, fmt, W, stream=None):
     return _check(lib().tri_unpack(_ptr(Wp), int(N), int(K), int(fmt), _ptr(W), _stream(stream)), "tri_unpack")
+
+
+def tri_quantize_workspace_bytes(N, K):
+    return int(lib().tri_quantize_workspace_bytes(int(N), int(K)))
+
+
+def tri_quantize(W, N, K, fmt, Wp, scale_out, workspace, workspace_bytes, stream=None):
+    return _check(lib().tri_quantize(_ptr(W), int(N), int(K), int(fmt), _ptr(Wp), _ptr(scale_out), _ptr(workspace),
+                                     int(workspace_bytes), _stream(stream)), "tri_quantize")
 
 
 def tri_linear(X, Wp, scale, M, N, K, fmt, Y, stream=None):
@@ -163,6 +177,20 @@ def unpack(Wp, K, fmt, stream=None):
     W = torch.empty((N, K), dtype=torch.int8, device=Wp.device)
     tri_unpack(Wp, N, K, fmt, W, stream)
     return W
+
+
+def quantize(W, fmt, stream=None):
+    """Quantise a (N, K) float32 CUDA tensor of latent weights; returns (packed weights as a new
+    (N, row_bytes) uint8 tensor, the scale as a new 1-element float32 tensor on the device)."""
+    import torch
+    N, K = W.shape
+    assert W.dtype == torch.float32 and W.is_cuda and W.is_contiguous()
+    Wp = torch.empty((N, tri_row_bytes(K, fmt)), dtype=torch.uint8, device=W.device)
+    scale = torch.empty(1, dtype=torch.float32, device=W.device)
+    nbytes = tri_quantize_workspace_bytes(N, K)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=W.device)
+    tri_quantize(W, N, K, fmt, Wp, scale, ws, nbytes, stream)
+    return Wp, scale
 
 
 def linear(X, Wp, scale, K, fmt, algo=TRI_ALGO_AUTO, out=None, stream=None):

@@ -59,6 +59,23 @@ extern "C" {
 
 int64_t tri_row_bytes(int64_t K, int fmt) { return row_bytes(K, fmt); }
 
+int64_t tri_quantize_workspace_bytes(int64_t N, int64_t K)
+{
+    if (N < 1 || K < 1 || N >= kMaxDim || K >= kMaxDim) return -1;
+    return quant_workspace_bytes(N * K);
+}
+
+int tri_quantize(const float *W, int64_t N, int64_t K, int fmt, uint8_t *Wp, float *scale_out, void *workspace,
+                 int64_t workspace_bytes, hipStream_t stream)
+{
+    if (!W || !Wp || !scale_out || !workspace || !known_fmt(fmt)) return TRI_EINVAL;
+    if (N < 1 || K < 1 || N >= kMaxDim || K >= kMaxDim) return TRI_EINVAL;
+    if (workspace_bytes < quant_workspace_bytes(N * K)) return TRI_EINVAL;
+    if (misaligned(W) || misaligned(Wp) || misaligned(workspace) || (reinterpret_cast<uintptr_t>(scale_out) & 3u))
+        return TRI_EALIGN;
+    return launch_quantize(W, N, K, fmt, Wp, scale_out, workspace, stream);
+}
+
 int tri_pack2(const int8_t *W, int64_t N, int64_t K, uint8_t *Wp, hipStream_t stream)
 {
     const int rc = check_pack(W, N, K, Wp);

@@ -16,6 +16,10 @@ inline int64_t row_bytes(int64_t K, int fmt)
 
 int launch_pack(const int8_t *W, int64_t N, int64_t K, int fmt, uint8_t *Wp, hipStream_t s);
 int launch_unpack(const uint8_t *Wp, int64_t N, int64_t K, int fmt, int8_t *W, hipStream_t s);
+// Quantiser (tri_quant.hip): workspace bytes for E = N*K weights, and the three launches.
+int64_t quant_workspace_bytes(int64_t E);
+int launch_quantize(const float *W, int64_t N, int64_t K, int fmt, uint8_t *Wp, float *scale, void *workspace,
+                    hipStream_t s);
 
 // Weight matrices that read the same activations, served by one launch (a grouped layer):
 // matrix g has N[g] rows and owns the 16-row blocks blk[g] .. blk[g+1]-1 of the grid.  A

@@ -3,17 +3,19 @@
 This module only draws random numbers: it holds none of the layer's arithmetic,
 so both the HIP path and the CPU oracle may use it.  Every draw comes from
 numpy's PCG64 generator seeded with ``[workload_id, layer_id, stream_id]``
-(stream 0 = weights, 1 = activations, 2 = scale).
+(stream 0 = weights, 1 = activations, 2 = scale, 3 = latent weights).
 
 Distributions (the ternary linear layer of a TriLM, weights in {-1, 0, +1}
 times one shared fp32 scale, fp16 activations):
   * trits: P(-1) = P(+1) = 0.3, P(0) = 0.4, int8, one (N, K) matrix per layer;
   * activations: N(0, 1) drawn in float32 and rounded to fp16 (round to nearest even);
-  * scale: a fixed value, or U(0.01, 0.05) rounded to fp32.
+  * scale: a fixed value, or U(0.01, 0.05) rounded to fp32;
+  * latent (full-precision) weights for the quantiser: N(0, std^2) in float32, std 0.02 by
+    default (a common initialisation scale of transformer linear layers).
 """
 import numpy as np
 
-STREAM_W, STREAM_X, STREAM_SCALE = 0, 1, 2
+STREAM_W, STREAM_X, STREAM_SCALE, STREAM_LATENT = 0, 1, 2, 3
 
 
 def rng_for(workload_id, layer_id, stream_id):
@@ -48,3 +50,13 @@ def layer_inputs(workload_id, layer_id, M, N, K, scale=None):
     X = activations(rng_for(workload_id, layer_id, STREAM_X), M, K)
     s = float(np.float32(scale)) if scale is not None else uniform_scale(rng_for(workload_id, layer_id, STREAM_SCALE))
     return W, X, s
+
+
+def latent_weights(rng, N, K, std=0.02, chunk_rows=1024):
+    """(N, K) float32 ~ N(0, std^2), drawn in float32 row-chunk by row-chunk."""
+    out = np.empty((N, K), dtype=np.float32)
+    for r0 in range(0, N, chunk_rows):
+        r1 = min(N, r0 + chunk_rows)
+        out[r0:r1] = rng.standard_normal((r1 - r0, K), dtype=np.float32)
+    out *= np.float32(std)
+    return out

@@ -83,6 +83,29 @@ int tri_pack16(const int8_t *W, int64_t N, int64_t K, uint8_t *Wp, hipStream_t s
  * Errors: TRI_EINVAL, TRI_EALIGN (Wp), TRI_EHIP. */
 int tri_unpack(const uint8_t *Wp, int64_t N, int64_t K, int fmt, int8_t *W, hipStream_t stream);
 
+/* Workspace (device bytes, a multiple of 8) that tri_quantize needs for an N x K
+ * matrix; -1 if N or K is < 1 or >= 2^31.  It depends on N*K only. */
+int64_t tri_quantize_workspace_bytes(int64_t N, int64_t K);
+
+/* Quantise latent full-precision weights to trits and one scale, and pack them
+ * (Pith review, "What carries the argument": latent full-precision weights rounded
+ * on the fly to {-1,0,1} times one shared scale; the review's domain assumptions:
+ * round-to-nearest).  The pages do not give the scale rule; the one taken is
+ *     scale = float32( sum_{n,k} |W[n][k]| / (N*K) )   (summed in float64),
+ *     t     = round_half_to_even(W / scale) clipped to [-1, 1]; 0 when scale == 0,
+ * so a weight becomes sign(w) exactly when 2|w| > scale, ties giving 0.
+ * W: N*K float32 row-major, 16-byte aligned, finite (non-finite weights give an
+ * unspecified scale and trits).  Wp: N*tri_row_bytes(K, fmt) bytes, 16-byte
+ * aligned, written as tri_pack2 / tri_pack16 would pack the trits.  scale_out: one
+ * float, 4-byte aligned, written on the stream (read it after synchronising).
+ * workspace: at least tri_quantize_workspace_bytes(N, K) bytes, 16-byte aligned,
+ * owned by the caller, overwritten; calls that share a workspace must be ordered
+ * on one stream.  W must not alias Wp, scale_out or workspace.
+ * Errors: TRI_EINVAL (a size < 1 or >= 2^31, null, unknown fmt, workspace too
+ * small), TRI_EALIGN, TRI_EHIP. */
+int tri_quantize(const float *W, int64_t N, int64_t K, int fmt, uint8_t *Wp, float *scale_out,
+                 void *workspace, int64_t workspace_bytes, hipStream_t stream);
+
 /* The ternary linear layer (Pith review, "What carries the argument"):
  *   Y[m][n] = fp16_rne(scale * sum_k t[n][k] * X[m][k]), fp32 accumulation.
  * X: M*K fp16 row-major (row stride K); Wp: packed weights as above; Y: M*N fp16

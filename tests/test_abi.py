@@ -126,3 +126,25 @@ def test_grouped_argument_errors_launch_nothing():
     assert raw("tri_linear_grouped", A, wp, sc, 1, ints(4, 0), 64, F2, yy, 2, s) == tri.TRI_EINVAL
     assert raw("tri_linear_grouped", A, wp, sc, 1, nn, 64, F2, ptrs(C, None), 2, s) == tri.TRI_EINVAL
     assert raw("tri_linear_grouped", None, wp, sc, 1, nn, 64, F2, yy, 2, s) == tri.TRI_EINVAL
+
+
+def test_quantize_workspace_and_argument_errors_launch_nothing():
+    F2 = tri.TRI_FMT_2BIT
+    s = None
+    assert tri.tri_quantize_workspace_bytes(0, 5) == -1
+    assert tri.tri_quantize_workspace_bytes(5, 0) == -1
+    assert tri.tri_quantize_workspace_bytes(1, 1) == 8
+    assert tri.tri_quantize_workspace_bytes(28672, 8192) == 8 * 2048
+    need = tri.tri_quantize_workspace_bytes(4, 64)
+    assert raw("tri_quantize", None, 4, 64, F2, B, C, A, need, s) == tri.TRI_EINVAL
+    assert raw("tri_quantize", A, 4, 64, F2, None, C, A, need, s) == tri.TRI_EINVAL
+    assert raw("tri_quantize", A, 4, 64, F2, B, None, A, need, s) == tri.TRI_EINVAL
+    assert raw("tri_quantize", A, 4, 64, F2, B, C, None, need, s) == tri.TRI_EINVAL
+    assert raw("tri_quantize", A, 4, 64, 2, B, C, A, need, s) == tri.TRI_EINVAL
+    for (N, K) in [(0, 64), (4, 0), (1 << 31, 64), (4, 1 << 31)]:
+        assert raw("tri_quantize", A, N, K, F2, B, C, A, 1 << 20, s) == tri.TRI_EINVAL
+    assert raw("tri_quantize", A, 4, 64, F2, B, C, A, need - 8, s) == tri.TRI_EINVAL
+    assert raw("tri_quantize", ODD, 4, 64, F2, B, C, A, need, s) == tri.TRI_EALIGN
+    assert raw("tri_quantize", A, 4, 64, F2, ODD, C, A, need, s) == tri.TRI_EALIGN
+    assert raw("tri_quantize", A, 4, 64, F2, B, C + 2, A, need, s) == tri.TRI_EALIGN
+    assert raw("tri_quantize", A, 4, 64, F2, B, C, ODD, need, s) == tri.TRI_EALIGN
