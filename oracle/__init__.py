@@ -2,7 +2,8 @@
 
 This package wraps ``tri_oracle.c``: a plain, slow, scalar C implementation of
 the 2-bit and 1.6-bit packings, their inverse, the ternary linear layer
-``Y = scale * (X @ W.T)`` summed in float64, and the quantiser from latent
+``Y = scale * (X @ W.T)`` summed in float64 (also with a decode block's glue --
+SiLU-gate, RMSNorm, residual -- folded around it), and the quantiser from latent
 float32 weights to trits and a scale.  It exists to check the HIP library,
 and only the test suite, the smoke check and the CPU-baseline leg of the
 benchmark may import it.  It shares no code with the HIP library (the only
@@ -67,6 +68,9 @@ def _load():
         lib.oracle_linear_f64.restype = ctypes.c_int
         lib.oracle_quantize.argtypes = [p, i64, i64, p, p]
         lib.oracle_quantize.restype = ctypes.c_int
+        lib.oracle_linear_fused_f64.argtypes = [p, p, ctypes.c_int, p, ctypes.c_double, p, ctypes.c_double, p,
+                                                i64, i64, i64, p]
+        lib.oracle_linear_fused_f64.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -155,6 +159,36 @@ def quantize(W):
     if N and K and _load().oracle_quantize(_ptr(W), N, K, _ptr(T), _ptr(s)) != 0:
         raise ValueError("non-finite weight")
     return T, np.float32(s[0])
+
+
+def linear_fused_f64(X, W, scale, gate=None, norm=False, gain=None, eps=1e-5, residual=None):
+    """The layer with block glue folded around it, in float64, unrounded:
+    x1 = silu(gate) * X (if gate), x2 = x1 * gain / sqrt(mean(x1^2) + eps) (if norm; gain None = 1),
+    Y = residual + scale * x2 @ W.T (residual None = 0).  X, gate: (M, K) fp16; gain: (K,) fp16;
+    residual: (M, N) fp16; W: (N, K) int8.  Returns (M, N) float64."""
+    X = np.ascontiguousarray(X, dtype=np.float16)
+    W = np.ascontiguousarray(W, dtype=np.int8)
+    M, K = X.shape
+    N, K2 = W.shape
+    if K != K2:
+        raise ValueError("K mismatch")
+    g = None if gate is None else np.ascontiguousarray(gate, dtype=np.float16)
+    if g is not None and g.shape != (M, K):
+        raise ValueError("gate shape")
+    gn = None if gain is None else np.ascontiguousarray(gain, dtype=np.float16).reshape(-1)
+    if gn is not None and gn.shape != (K,):
+        raise ValueError("gain shape")
+    r = None if residual is None else np.ascontiguousarray(residual, dtype=np.float16)
+    if r is not None and r.shape != (M, N):
+        raise ValueError("residual shape")
+    Y = np.empty((M, N), dtype=np.float64)
+    opt = lambda a: None if a is None else _ptr(a.view(np.uint16))
+    if M and N:
+        rc = _load().oracle_linear_fused_f64(_ptr(X.view(np.uint16)), opt(g), int(bool(norm)), opt(gn), float(eps),
+                                             _ptr(W), float(scale), opt(r), M, N, K, _ptr(Y))
+        if rc != 0:
+            raise ValueError("non-finite input")
+    return Y
 
 
 def max_threads():

@@ -40,6 +40,9 @@
  *     243..255 go through the same repeated division by 3;
  *   - the layer returns scale * sum_k t[n][k] * x[m][k] exactly as summed in
  *     float64 in k order, unrounded;
+ *   - the block glue folded around a layer (the pages name the block's parts, not
+ *     their placement): SiLU-gate before RMSNorm before the product, the residual
+ *     added to the scaled sum, all in float64;
  *   - the quantiser's scale (the pages do not give its rule) is the mean absolute
  *     value of the matrix, summed in float64 and rounded once to float32; a weight
  *     becomes round-half-to-even(w / scale) clipped to [-1, 1], and a zero scale
@@ -50,6 +53,7 @@
 #include <stdint.h>
 #include <stddef.h>
 #include <math.h>
+#include <stdlib.h>
 #ifdef _OPENMP
 #include <omp.h>
 #endif
@@ -221,6 +225,56 @@ int oracle_quantize(const float *W, int64_t N, int64_t K, int8_t *T, float *scal
             if (q < -1.0) q = -1.0;
         }
         T[i] = (int8_t)q;
+    }
+    return 0;
+}
+
+/* The ternary linear layer with the glue of a decode block folded around it
+ * ([PR] "If this is right": the end-to-end speed-up falls short of the layer's
+ * because of the work outside the linear layers).  For activation row m, in float64
+ * and unrounded:
+ *   x1[k] = gate ? silu(gate[m][k]) * x[m][k] : x[m][k],   silu(z) = z / (1 + exp(-z));
+ *   x2[k] = norm ? x1[k] * gain[k] / sqrt(mean_k(x1[k]^2) + eps) : x1[k]
+ *           (gain NULL: a gain of 1);
+ *   Y[m][n] = (residual ? residual[m][n] : 0) + scale * sum_k t[n][k] * x2[k].
+ * X, gate: M*K fp16 bit patterns; gain: K fp16 bit patterns; residual: M*N fp16 bit
+ * patterns; W: N*K trits; Y: M*N float64.  Returns 0, or -1 on a non-finite input. */
+int oracle_linear_fused_f64(const uint16_t *X, const uint16_t *gate, int norm, const uint16_t *gain, double eps,
+                            const int8_t *W, double scale, const uint16_t *residual,
+                            int64_t M, int64_t N, int64_t K, double *Y)
+{
+    for (int64_t i = 0; i < M * K; ++i) {
+        if (!isfinite(oracle_half_to_double(X[i]))) return -1;
+        if (gate && !isfinite(oracle_half_to_double(gate[i]))) return -1;
+    }
+    for (int64_t k = 0; gain && k < K; ++k)
+        if (!isfinite(oracle_half_to_double(gain[k]))) return -1;
+    for (int64_t i = 0; residual && i < M * N; ++i)
+        if (!isfinite(oracle_half_to_double(residual[i]))) return -1;
+    for (int64_t m = 0; m < M; ++m) {
+        double *x = (double *)malloc((size_t)K * sizeof(double));
+        if (!x) return -1;
+        for (int64_t k = 0; k < K; ++k) {
+            double v = oracle_half_to_double(X[m * K + k]);
+            if (gate) {
+                double z = oracle_half_to_double(gate[m * K + k]);
+                v = z / (1.0 + exp(-z)) * v;
+            }
+            x[k] = v;
+        }
+        if (norm) {
+            double sq = 0.0;
+            for (int64_t k = 0; k < K; ++k) sq += x[k] * x[k];
+            double r = sqrt(sq / (double)K + eps);
+            for (int64_t k = 0; k < K; ++k)
+                x[k] = x[k] * (gain ? oracle_half_to_double(gain[k]) : 1.0) / r;
+        }
+        for (int64_t n = 0; n < N; ++n) {
+            double sum = 0.0;
+            for (int64_t k = 0; k < K; ++k) sum += (double)W[n * K + k] * x[k];
+            Y[m * N + n] = (residual ? oracle_half_to_double(residual[m * N + n]) : 0.0) + scale * sum;
+        }
+        free(x);
     }
     return 0;
 }

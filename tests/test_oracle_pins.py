@@ -341,3 +341,77 @@ def test_quantize_zero_fraction_of_gaussian_weights():
     assert abs(np.mean(T == 0) - p0) < 3e-3
     assert abs(np.mean(T == 1) - (1 - p0) / 2) < 3e-3
     assert abs(float(s) - 0.02 * math.sqrt(2.0 / math.pi)) < 1e-4
+
+
+# ---------------------------------------------------------------- the layer with block glue folded around it
+# With W the identity (t[n][k] = 1 if n == k) and scale 1, Y is the layer's effective input itself,
+# so the glue can be checked against closed forms without re-typing it.
+
+def identity(K):
+    return np.eye(K, dtype=np.int8)
+
+
+def test_fused_without_glue_is_the_plain_layer():
+    rng = synth.rng_for(970, 0, 0)
+    W = synth.trits(rng, 11, 97)
+    X = synth.activations(rng, 3, 97)
+    np.testing.assert_array_equal(oracle.linear_fused_f64(X, W, 0.02), oracle.linear_f64(X, W, 0.02))
+
+
+def test_fused_rmsnorm_normalises_rows():
+    rng = synth.rng_for(971, 0, 0)
+    K = 64
+    X = synth.activations(rng, 4, K)
+    Y = oracle.linear_fused_f64(X, identity(K), 1.0, norm=True, eps=0.0)
+    np.testing.assert_allclose(np.mean(Y * Y, axis=1), 1.0, rtol=1e-12)            # unit mean square
+    ratio = Y / X.astype(np.float64)                                              # a positive factor per row
+    assert np.all(ratio > 0)
+    np.testing.assert_allclose(ratio, ratio[:, :1] * np.ones((1, K)), rtol=1e-12)
+    # a constant row c: x / sqrt(c^2 + eps)
+    Xc = np.full((1, K), 0.5, np.float16)
+    Yc = oracle.linear_fused_f64(Xc, identity(K), 1.0, norm=True, eps=0.25)
+    np.testing.assert_allclose(Yc, 0.5 / math.sqrt(0.25 + 0.25), rtol=1e-15)
+    # a power-of-two rescaling of the input changes nothing (eps = 0)
+    np.testing.assert_array_equal(oracle.linear_fused_f64(X * np.float16(4), identity(K), 1.0, norm=True, eps=0.0), Y)
+    # the gain multiplies feature k
+    gain = np.linspace(-2, 2, K).astype(np.float16)
+    Yg = oracle.linear_fused_f64(X, identity(K), 1.0, norm=True, eps=0.0, gain=gain)
+    np.testing.assert_allclose(Yg, Y * gain.astype(np.float64), rtol=1e-15, atol=1e-300)
+
+
+def test_fused_silu_gate_closed_forms():
+    z = np.array([[0.0, math.log(3.0), -math.log(3.0), 2.0, -2.0, 12.0]], np.float16)
+    z64 = z.astype(np.float64)[0]
+    X = np.ones((1, 6), np.float16)
+    Y = oracle.linear_fused_f64(X, identity(6), 1.0, gate=z)[0]
+    assert Y[0] == 0.0                                                         # silu(0) = 0
+    # silu(z) = z * sigmoid(z), sigmoid(ln 3) = 3/4 (z rounded to fp16 first)
+    np.testing.assert_allclose(Y[1], z64[1] / (1 + 1 / 3.0 * math.exp(math.log(3.0) - z64[1])), rtol=1e-12)
+    assert abs(Y[1] - 0.75 * z64[1]) < 1e-3
+    # silu(z) - silu(-z) = z, since sigmoid(z) + sigmoid(-z) = 1
+    assert abs((Y[1] - Y[2]) - z64[1]) < 1e-14
+    assert abs((Y[3] - Y[4]) - 2.0) < 1e-14
+    assert abs(Y[5] - 12.0) < 1e-4                                              # silu(z) -> z for large z
+    # the gate multiplies the activation
+    X2 = np.array([[1, -3, 0.5, 2, 2, 1]], np.float16)
+    Y2 = oracle.linear_fused_f64(X2, identity(6), 1.0, gate=z)[0]
+    np.testing.assert_allclose(Y2, Y * X2.astype(np.float64)[0], rtol=1e-15)
+
+
+def test_fused_residual_and_order_of_glue():
+    rng = synth.rng_for(972, 0, 0)
+    M, N, K = 2, 5, 40
+    X = synth.activations(rng, M, K)
+    R = synth.activations(rng, M, N)
+    # zero weights leave exactly the residual
+    np.testing.assert_array_equal(oracle.linear_fused_f64(X, np.zeros((N, K), np.int8), 0.7, residual=R),
+                                  R.astype(np.float64))
+    # the gate is applied before the norm: gating by a constant c cancels in the norm (eps = 0)
+    G = np.full((M, K), 3.0, np.float16)
+    Y1 = oracle.linear_fused_f64(X, identity(K), 1.0, norm=True, eps=0.0)
+    Y2 = oracle.linear_fused_f64(X, identity(K), 1.0, norm=True, eps=0.0, gate=G)
+    np.testing.assert_allclose(Y2, Y1, rtol=1e-13)
+    with pytest.raises(ValueError):
+        bad = G.copy()
+        bad[0, 0] = np.inf
+        oracle.linear_fused_f64(X, identity(K), 1.0, gate=bad)
