@@ -3,8 +3,8 @@
 This package wraps ``tri_oracle.c``: a plain, slow, scalar C implementation of
 the 2-bit and 1.6-bit packings, their inverse, the ternary linear layer
 ``Y = scale * (X @ W.T)`` summed in float64 (also with a decode block's glue --
-SiLU-gate, RMSNorm, residual -- folded around it), and the quantiser from latent
-float32 weights to trits and a scale.  It exists to check the HIP library,
+RMSNorm, residual, SiLU gate of two layers -- folded around it), and the quantiser
+from latent float32 weights to trits and a scale.  It exists to check the HIP library,
 and only the test suite, the smoke check and the CPU-baseline leg of the
 benchmark may import it.  It shares no code with the HIP library (the only
 common module is the seeded input generator, which holds none of the layer's
@@ -68,8 +68,10 @@ def _load():
         lib.oracle_linear_f64.restype = ctypes.c_int
         lib.oracle_quantize.argtypes = [p, i64, i64, p, p]
         lib.oracle_quantize.restype = ctypes.c_int
-        lib.oracle_linear_fused_f64.argtypes = [p, p, ctypes.c_int, p, ctypes.c_double, p, ctypes.c_double, p,
+        lib.oracle_linear_fused_f64.argtypes = [p, ctypes.c_int, p, ctypes.c_double, p, ctypes.c_double, p,
                                                 i64, i64, i64, p]
+        lib.oracle_silu_mul_f64.argtypes = [p, p, i64, p]
+        lib.oracle_silu_mul_f64.restype = None
         lib.oracle_linear_fused_f64.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
@@ -161,10 +163,10 @@ def quantize(W):
     return T, np.float32(s[0])
 
 
-def linear_fused_f64(X, W, scale, gate=None, norm=False, gain=None, eps=1e-5, residual=None):
+def linear_fused_f64(X, W, scale, norm=False, gain=None, eps=1e-5, residual=None):
     """The layer with block glue folded around it, in float64, unrounded:
-    x1 = silu(gate) * X (if gate), x2 = x1 * gain / sqrt(mean(x1^2) + eps) (if norm; gain None = 1),
-    Y = residual + scale * x2 @ W.T (residual None = 0).  X, gate: (M, K) fp16; gain: (K,) fp16;
+    x2 = X * gain / sqrt(mean(X^2) + eps) per row (if norm; gain None = 1),
+    Y = residual + scale * x2 @ W.T (residual None = 0).  X: (M, K) fp16; gain: (K,) fp16;
     residual: (M, N) fp16; W: (N, K) int8.  Returns (M, N) float64."""
     X = np.ascontiguousarray(X, dtype=np.float16)
     W = np.ascontiguousarray(W, dtype=np.int8)
@@ -172,9 +174,6 @@ def linear_fused_f64(X, W, scale, gate=None, norm=False, gain=None, eps=1e-5, re
     N, K2 = W.shape
     if K != K2:
         raise ValueError("K mismatch")
-    g = None if gate is None else np.ascontiguousarray(gate, dtype=np.float16)
-    if g is not None and g.shape != (M, K):
-        raise ValueError("gate shape")
     gn = None if gain is None else np.ascontiguousarray(gain, dtype=np.float16).reshape(-1)
     if gn is not None and gn.shape != (K,):
         raise ValueError("gain shape")
@@ -184,11 +183,31 @@ def linear_fused_f64(X, W, scale, gate=None, norm=False, gain=None, eps=1e-5, re
     Y = np.empty((M, N), dtype=np.float64)
     opt = lambda a: None if a is None else _ptr(a.view(np.uint16))
     if M and N:
-        rc = _load().oracle_linear_fused_f64(_ptr(X.view(np.uint16)), opt(g), int(bool(norm)), opt(gn), float(eps),
+        rc = _load().oracle_linear_fused_f64(_ptr(X.view(np.uint16)), int(bool(norm)), opt(gn), float(eps),
                                              _ptr(W), float(scale), opt(r), M, N, K, _ptr(Y))
         if rc != 0:
             raise ValueError("non-finite input")
     return Y
+
+
+def silu_mul_f64(a, b):
+    """silu(a) * b elementwise in float64, silu(z) = z / (1 + exp(-z))."""
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    b = np.ascontiguousarray(b, dtype=np.float64)
+    if a.shape != b.shape:
+        raise ValueError("shape mismatch")
+    out = np.empty_like(a)
+    if a.size:
+        _load().oracle_silu_mul_f64(_ptr(a), _ptr(b), a.size, _ptr(out))
+    return out
+
+
+def silu_pair_f64(X, W_gate, scale_gate, W_up, scale_up, norm=False, gain=None, eps=1e-5):
+    """The gated-MLP input of a block: silu(gate layer) * (up layer), both layers on the same
+    (optionally RMS-normalised) activations, in float64, unrounded.  Returns (M, N) float64."""
+    a = linear_fused_f64(X, W_gate, scale_gate, norm=norm, gain=gain, eps=eps)
+    b = linear_fused_f64(X, W_up, scale_up, norm=norm, gain=gain, eps=eps)
+    return silu_mul_f64(a, b)
 
 
 def max_threads():

@@ -41,8 +41,9 @@
  *   - the layer returns scale * sum_k t[n][k] * x[m][k] exactly as summed in
  *     float64 in k order, unrounded;
  *   - the block glue folded around a layer (the pages name the block's parts, not
- *     their placement): SiLU-gate before RMSNorm before the product, the residual
- *     added to the scaled sum, all in float64;
+ *     their placement): RMSNorm of the input before the product, the residual added
+ *     to the scaled sum, the SiLU gate applied to two layers' unrounded outputs, all
+ *     in float64;
  *   - the quantiser's scale (the pages do not give its rule) is the mean absolute
  *     value of the matrix, summed in float64 and rounded once to float32; a weight
  *     becomes round-half-to-even(w / scale) clipped to [-1, 1], and a zero scale
@@ -233,35 +234,25 @@ int oracle_quantize(const float *W, int64_t N, int64_t K, int8_t *T, float *scal
  * ([PR] "If this is right": the end-to-end speed-up falls short of the layer's
  * because of the work outside the linear layers).  For activation row m, in float64
  * and unrounded:
- *   x1[k] = gate ? silu(gate[m][k]) * x[m][k] : x[m][k],   silu(z) = z / (1 + exp(-z));
- *   x2[k] = norm ? x1[k] * gain[k] / sqrt(mean_k(x1[k]^2) + eps) : x1[k]
+ *   x2[k] = norm ? x[m][k] * gain[k] / sqrt(mean_k(x[m][k]^2) + eps) : x[m][k]
  *           (gain NULL: a gain of 1);
  *   Y[m][n] = (residual ? residual[m][n] : 0) + scale * sum_k t[n][k] * x2[k].
- * X, gate: M*K fp16 bit patterns; gain: K fp16 bit patterns; residual: M*N fp16 bit
+ * X: M*K fp16 bit patterns; gain: K fp16 bit patterns; residual: M*N fp16 bit
  * patterns; W: N*K trits; Y: M*N float64.  Returns 0, or -1 on a non-finite input. */
-int oracle_linear_fused_f64(const uint16_t *X, const uint16_t *gate, int norm, const uint16_t *gain, double eps,
+int oracle_linear_fused_f64(const uint16_t *X, int norm, const uint16_t *gain, double eps,
                             const int8_t *W, double scale, const uint16_t *residual,
                             int64_t M, int64_t N, int64_t K, double *Y)
 {
-    for (int64_t i = 0; i < M * K; ++i) {
+    for (int64_t i = 0; i < M * K; ++i)
         if (!isfinite(oracle_half_to_double(X[i]))) return -1;
-        if (gate && !isfinite(oracle_half_to_double(gate[i]))) return -1;
-    }
     for (int64_t k = 0; gain && k < K; ++k)
         if (!isfinite(oracle_half_to_double(gain[k]))) return -1;
     for (int64_t i = 0; residual && i < M * N; ++i)
         if (!isfinite(oracle_half_to_double(residual[i]))) return -1;
+    double *x = (double *)malloc((size_t)K * sizeof(double));
+    if (!x) return -1;
     for (int64_t m = 0; m < M; ++m) {
-        double *x = (double *)malloc((size_t)K * sizeof(double));
-        if (!x) return -1;
-        for (int64_t k = 0; k < K; ++k) {
-            double v = oracle_half_to_double(X[m * K + k]);
-            if (gate) {
-                double z = oracle_half_to_double(gate[m * K + k]);
-                v = z / (1.0 + exp(-z)) * v;
-            }
-            x[k] = v;
-        }
+        for (int64_t k = 0; k < K; ++k) x[k] = oracle_half_to_double(X[m * K + k]);
         if (norm) {
             double sq = 0.0;
             for (int64_t k = 0; k < K; ++k) sq += x[k] * x[k];
@@ -274,9 +265,16 @@ int oracle_linear_fused_f64(const uint16_t *X, const uint16_t *gate, int norm, c
             for (int64_t k = 0; k < K; ++k) sum += (double)W[n * K + k] * x[k];
             Y[m * N + n] = (residual ? oracle_half_to_double(residual[m * N + n]) : 0.0) + scale * sum;
         }
-        free(x);
     }
+    free(x);
     return 0;
+}
+
+/* The SiLU gate of a gated MLP applied to two layer outputs: out[i] = silu(a[i]) * b[i],
+ * silu(z) = z / (1 + exp(-z)), in float64. */
+void oracle_silu_mul_f64(const double *a, const double *b, int64_t n, double *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = a[i] / (1.0 + exp(-a[i])) * b[i];
 }
 
 /* Number of OpenMP threads a parallel region would use (1 without OpenMP). */

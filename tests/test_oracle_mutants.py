@@ -39,13 +39,13 @@ MUTANTS = [
     ("quantise not clipped", "if (q > 1.0) q = 1.0;", ";"),
     ("quantise mean over K only", "(double)N * (double)K", "(double)K"),
     ("quantise sign flipped", "T[i] = (int8_t)q;", "T[i] = (int8_t)-q;"),
-    ("fused: silu as sigmoid", "v = z / (1.0 + exp(-z)) * v;", "v = 1.0 / (1.0 + exp(-z)) * v;"),
+    ("silu as sigmoid", "out[i] = a[i] / (1.0 + exp(-a[i])) * b[i];", "out[i] = 1.0 / (1.0 + exp(-a[i])) * b[i];"),
+    ("silu gate without the up layer", "out[i] = a[i] / (1.0 + exp(-a[i])) * b[i];", "out[i] = a[i] / (1.0 + exp(-a[i]));"),
     ("fused: eps dropped", "double r = sqrt(sq / (double)K + eps);", "double r = sqrt(sq / (double)K);"),
     ("fused: mean over K-1", "double r = sqrt(sq / (double)K + eps);", "double r = sqrt(sq / (double)(K - 1) + eps);"),
     ("fused: gain ignored", "x[k] = x[k] * (gain ? oracle_half_to_double(gain[k]) : 1.0) / r;", "x[k] = x[k] / r;"),
     ("fused: residual dropped", "Y[m * N + n] = (residual ? oracle_half_to_double(residual[m * N + n]) : 0.0) + scale * sum;",
      "Y[m * N + n] = scale * sum;"),
-    ("fused: gate ignored", "            if (gate) {\n                double z", "            if (gate && 0) {\n                double z"),
     ("quantise threshold at the scale", "q = rint((double)W[i] / (double)s);", "q = rint((double)W[i] / (double)s / 2.0);"),
 ]
 

@@ -379,26 +379,39 @@ def test_fused_rmsnorm_normalises_rows():
     np.testing.assert_allclose(Yg, Y * gain.astype(np.float64), rtol=1e-15, atol=1e-300)
 
 
-def test_fused_silu_gate_closed_forms():
-    z = np.array([[0.0, math.log(3.0), -math.log(3.0), 2.0, -2.0, 12.0]], np.float16)
+def test_silu_closed_forms():
+    z = np.array([0.0, math.log(3.0), -math.log(3.0), 2.0, -2.0, 30.0, -30.0])
+    out = oracle.silu_mul_f64(z, np.ones_like(z))
+    assert out[0] == 0.0                                                       # silu(0) = 0
+    assert abs(out[1] - 0.75 * math.log(3.0)) < 1e-15                          # sigmoid(ln 3) = 3/4
+    assert abs((out[1] - out[2]) - math.log(3.0)) < 1e-15                      # silu(z) - silu(-z) = z
+    assert abs((out[3] - out[4]) - 2.0) < 1e-15
+    assert abs(out[5] - 30.0) < 1e-11 and abs(out[6]) < 1e-11                  # silu(z) -> max(z, 0)
+    b = np.array([1.0, -2.0, 0.5, 3.0, 3.0, 1.0, 1.0])
+    np.testing.assert_allclose(oracle.silu_mul_f64(z, b), out * b, rtol=1e-15)   # the gate scales b
+
+
+def test_silu_pair_with_identity_weights():
+    # gate and up layers both the identity: the output is silu(x) * x
+    z = np.array([[0.0, math.log(3.0), -math.log(3.0), 2.0]], np.float16)
     z64 = z.astype(np.float64)[0]
-    X = np.ones((1, 6), np.float16)
-    Y = oracle.linear_fused_f64(X, identity(6), 1.0, gate=z)[0]
-    assert Y[0] == 0.0                                                         # silu(0) = 0
-    # silu(z) = z * sigmoid(z), sigmoid(ln 3) = 3/4 (z rounded to fp16 first)
-    np.testing.assert_allclose(Y[1], z64[1] / (1 + 1 / 3.0 * math.exp(math.log(3.0) - z64[1])), rtol=1e-12)
-    assert abs(Y[1] - 0.75 * z64[1]) < 1e-3
-    # silu(z) - silu(-z) = z, since sigmoid(z) + sigmoid(-z) = 1
-    assert abs((Y[1] - Y[2]) - z64[1]) < 1e-14
-    assert abs((Y[3] - Y[4]) - 2.0) < 1e-14
-    assert abs(Y[5] - 12.0) < 1e-4                                              # silu(z) -> z for large z
-    # the gate multiplies the activation
-    X2 = np.array([[1, -3, 0.5, 2, 2, 1]], np.float16)
-    Y2 = oracle.linear_fused_f64(X2, identity(6), 1.0, gate=z)[0]
-    np.testing.assert_allclose(Y2, Y * X2.astype(np.float64)[0], rtol=1e-15)
+    out = oracle.silu_pair_f64(z, identity(4), 1.0, identity(4), 1.0)[0]
+    assert out[0] == 0.0
+    np.testing.assert_allclose(out[1], z64[1] * z64[1] / (1 + math.exp(-z64[1])), rtol=1e-15)
+    assert abs(out[1] - 0.75 * z64[1] ** 2) < 2e-3
+    # a gate scale of 0 gives silu(0) = 0 everywhere
+    assert not oracle.silu_pair_f64(z, identity(4), 0.0, identity(4), 1.0).any()
+    # the up scale multiplies the output
+    np.testing.assert_allclose(oracle.silu_pair_f64(z, identity(4), 1.0, identity(4), -3.0)[0], -3.0 * out,
+                               rtol=1e-15)
+    # normalised inputs: both layers see the same unit-mean-square activations
+    X = synth.activations(synth.rng_for(973, 0, 0), 2, 64)
+    n = oracle.linear_fused_f64(X, identity(64), 1.0, norm=True, eps=0.0)
+    np.testing.assert_allclose(oracle.silu_pair_f64(X, identity(64), 1.0, identity(64), 1.0, norm=True, eps=0.0),
+                               n / (1 + np.exp(-n)) * n, rtol=1e-14)
 
 
-def test_fused_residual_and_order_of_glue():
+def test_fused_residual_and_nonfinite_inputs():
     rng = synth.rng_for(972, 0, 0)
     M, N, K = 2, 5, 40
     X = synth.activations(rng, M, K)
@@ -406,12 +419,10 @@ def test_fused_residual_and_order_of_glue():
     # zero weights leave exactly the residual
     np.testing.assert_array_equal(oracle.linear_fused_f64(X, np.zeros((N, K), np.int8), 0.7, residual=R),
                                   R.astype(np.float64))
-    # the gate is applied before the norm: gating by a constant c cancels in the norm (eps = 0)
-    G = np.full((M, K), 3.0, np.float16)
-    Y1 = oracle.linear_fused_f64(X, identity(K), 1.0, norm=True, eps=0.0)
-    Y2 = oracle.linear_fused_f64(X, identity(K), 1.0, norm=True, eps=0.0, gate=G)
-    np.testing.assert_allclose(Y2, Y1, rtol=1e-13)
-    with pytest.raises(ValueError):
-        bad = G.copy()
-        bad[0, 0] = np.inf
-        oracle.linear_fused_f64(X, identity(K), 1.0, gate=bad)
+    # the residual adds to the scaled product
+    W = synth.trits(rng, N, K)
+    np.testing.assert_allclose(oracle.linear_fused_f64(X, W, 0.7, residual=R),
+                               oracle.linear_f64(X, W, 0.7) + R.astype(np.float64), rtol=1e-15, atol=1e-15)
+    for kw in (dict(residual=np.full((M, N), np.inf, np.float16)), dict(norm=True, gain=np.full(K, np.nan, np.float16))):
+        with pytest.raises(ValueError):
+            oracle.linear_fused_f64(X, W, 0.7, **kw)
