@@ -317,10 +317,37 @@ def bench_batched(clock):
     return res
 
 
+def graph_time(step, nsteps, replays=10):
+    """Mean GPU time (s) of one call of `step`: `nsteps` calls captured in a HIP graph, replayed."""
+    import torch
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(nsteps):
+                step()
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(replays):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    del g
+    return a.elapsed_time(b) / 1e3 / (replays * nsteps)
+
+
 def bench_block(clock):
     """One block decode step: Q, K, V, O (4096x4096), gate, up (4096->11008), down (11008->4096),
-    inputs pre-staged, weights rotating over copies.  Timed as seven launches and as four,
-    with Q/K/V and gate/up each as one grouped launch (they read the same activations)."""
+    inputs pre-staged, weights rotating over copies.  Timed as seven launches, as four (Q/K/V
+    and gate/up each one grouped launch: they read the same activations), and as the whole
+    block with its glue (RMSNorm, residuals, silu gate) folded into four fused launches.  The
+    bytes are those of the seven linears (the glue reads a few KB more).  Each variant is timed
+    as a replayed HIP graph, so no host time enters it."""
     import torch
     import bit_mixed_precision_tri_amd as tri
     from bit_mixed_precision_tri_amd import configs, synth
@@ -367,13 +394,38 @@ def bench_block(clock):
             one(6, Xm)
             ctr[0] += 1
 
-        t7, _ = clock.run([step7] * 50)
-        t4, _ = clock.run([step4] * 50)
+        # the whole block with its glue on the GPU, folded into four fused launches: RMSNorm into
+        # Q/K/V and into gate/up, the residual into O and down, the silu gate into the gate/up
+        # launch (one workgroup serves the same rows of both and writes silu(gate) * up)
+        Yq = [Ys[0], Ys[1], Ys[2]]
+        Yh = torch.empty((M, cfg["hidden"]), dtype=torch.float16, device="cuda")
+        Ya = torch.empty((M, cfg["mlp"]), dtype=torch.float16, device="cuda")
+        Yout = torch.empty_like(Yh)
+
+        def fused(ids, Xi, Ys_, norm=False, pair=False, res=None):
+            c = ctr[0] % copies
+            tri.tri_linear_fused(Xi, [pools[i][c] for i in ids], [scales[i] for i in ids], M, [Ns[i] for i in ids],
+                                 Ks[ids[0]], F, Ys_, norm=norm, eps=1e-5, pair=pair, residuals=res)
+
+        def step_glue():
+            fused([0, 1, 2], Xh, Yq, norm=True)
+            fused([3], Ys[2], [Yh], res=[Xh])
+            fused([4, 5], Yh, [Ya, None], norm=True, pair=True)
+            fused([6], Ya, [Yout], res=[Yh])
+            ctr[0] += 1
+
+        # each variant: a HIP graph of `copies` steps (every step on other weight copies), replayed
+        t7 = graph_time(step7, copies)
+        t4 = graph_time(step4, copies)
+        tg = graph_time(step_glue, copies)
         res.append({"M": M, "bytes": nbytes,
                     "separate": {"launches": 7, "step_us": round(t7 * 1e6, 3), "GBps": round(nbytes / t7 / 1e9, 1),
                                  "frac_hbm": round(nbytes / t7 / 1e9 / HBM_PEAK_GBS, 4)},
                     "grouped": {"launches": 4, "step_us": round(t4 * 1e6, 3), "GBps": round(nbytes / t4 / 1e9, 1),
-                                "frac_hbm": round(nbytes / t4 / 1e9 / HBM_PEAK_GBS, 4)}})
+                                "frac_hbm": round(nbytes / t4 / 1e9 / HBM_PEAK_GBS, 4)},
+                    "fused_with_glue": {"launches": 4, "step_us": round(tg * 1e6, 3),
+                                        "GBps": round(nbytes / tg / 1e9, 1),
+                                        "frac_hbm": round(nbytes / tg / 1e9 / HBM_PEAK_GBS, 4)}})
         del pools
         torch.cuda.empty_cache()
     return res

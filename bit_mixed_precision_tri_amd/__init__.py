@@ -23,6 +23,12 @@ ALGO_NAMES = {TRI_ALGO_GEMV: "gemv", TRI_ALGO_SMALLM: "smallm", TRI_ALGO_GEMM: "
 _lib = None
 
 
+class TriGlue(ctypes.Structure):
+    """tri_glue of include/tri.h."""
+    _fields_ = [("norm_gain", ctypes.c_void_p), ("norm", ctypes.c_int), ("norm_eps", ctypes.c_float),
+                ("pair", ctypes.c_int), ("residual", ctypes.c_void_p)]
+
+
 class TriError(RuntimeError):
     def __init__(self, code, what):
         super().__init__("%s failed: %s (%d)" % (what, status_string(code), code))
@@ -54,6 +60,8 @@ def lib():
         L.tri_linear_algo.restype = i32
         L.tri_linear_grouped.argtypes = [p, p, p, i64, p, i64, i32, p, i32, p]
         L.tri_linear_grouped.restype = i32
+        L.tri_linear_fused.argtypes = [p, p, p, i64, p, i64, i32, p, i32, ctypes.POINTER(TriGlue), p]
+        L.tri_linear_fused.restype = i32
         L.tri_select_algo.argtypes = [i64, i64, i64, i32]
         L.tri_select_algo.restype = i32
         L.tri_status_string.argtypes = [i32]
@@ -138,6 +146,27 @@ def tri_linear_grouped(X, Wps, scales, M, Ns, K, fmt, Ys, stream=None):
     yy = (ctypes.c_void_p * max(G, 1))(*[_ptr(y).value for y in Ys])
     return _check(lib().tri_linear_grouped(_ptr(X), wp, sc, int(M), nn, int(K), int(fmt), yy, int(G),
                                            _stream(stream)), "tri_linear_grouped")
+
+
+def tri_linear_fused(X, Wps, scales, M, Ns, K, fmt, Ys, norm=False, gain=None, eps=1e-5, pair=False,
+                     residuals=None, stream=None):
+    """tri_linear_grouped with a decode block's glue: y_g = scales[g] * x' W_g^T (x' = rmsnorm(X) if norm);
+    Ys[g] = fp16(residuals[g] + y_g), or with pair (two matrices, gate then up) Ys[0] = fp16(residuals[0] +
+    silu(y_0) * y_1).  residuals: None or a sequence of G entries (tensor or None); Ys[1] may be None with pair."""
+    G = len(Wps)
+    if not (len(scales) == len(Ns) == len(Ys) == G) or (residuals is not None and len(residuals) != G):
+        raise ValueError("tri_linear_fused: per-matrix sequences must have the same length")
+    wp = (ctypes.c_void_p * max(G, 1))(*[_ptr(w).value for w in Wps])
+    sc = (ctypes.c_float * max(G, 1))(*[float(v) for v in scales])
+    nn = (ctypes.c_int64 * max(G, 1))(*[int(v) for v in Ns])
+    yy = (ctypes.c_void_p * max(G, 1))(*[None if y is None else _ptr(y).value for y in Ys])
+    rr = None
+    if residuals is not None:
+        rr = (ctypes.c_void_p * max(G, 1))(*[None if r is None else _ptr(r).value for r in residuals])
+    glue = TriGlue(None if gain is None else _ptr(gain).value, 1 if norm else 0, float(eps), 1 if pair else 0,
+                   None if rr is None else ctypes.cast(rr, ctypes.c_void_p).value)
+    return _check(lib().tri_linear_fused(_ptr(X), wp, sc, int(M), nn, int(K), int(fmt), yy, int(G),
+                                         ctypes.byref(glue), _stream(stream)), "tri_linear_fused")
 
 
 def tri_select_algo(M, N, K, fmt):

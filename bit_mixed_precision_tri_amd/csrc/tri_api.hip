@@ -148,6 +148,49 @@ int tri_linear_grouped(const _Float16 *X, const uint8_t *const *Wp, const float 
     return TRI_OK;
 }
 
+int tri_linear_fused(const _Float16 *X, const uint8_t *const *Wp, const float *scale, int64_t M, const int64_t *N,
+                     int64_t K, int fmt, _Float16 *const *Y, int G, const tri_glue *glue, hipStream_t stream)
+{
+    if (!glue || !Wp || !scale || !N || !Y || G < 1 || G > TRI_MAX_GROUPS) return TRI_EINVAL;
+    const bool pair = glue->pair != 0;
+    if (pair && (G != 2 || N[0] != N[1])) return TRI_EINVAL;
+    for (int g = 0; g < G; ++g) {
+        const int rc = check_linear(X, Wp[g], M, N[g], K, fmt, (pair && g == 1) ? Y[0] : Y[g]);
+        if (rc != TRI_OK) return rc;
+    }
+    if (M > 16 || (K % 8) != 0) return TRI_EINVAL;
+    if ((glue->norm || pair) && K > (fmt == TRI_FMT_2BIT ? 16384 : 20480)) return TRI_EINVAL;
+    int64_t blocks = 0;
+    for (int g = 0; g < G; ++g) blocks += (N[g] + 15) / 16;
+    if (blocks >= ((int64_t)1 << 31)) return TRI_EINVAL;
+    if (glue->norm && !(glue->norm_eps >= 0.f && glue->norm_eps <= 3.4e38f)) return TRI_EINVAL;   // (NaN fails)
+    if (misaligned(glue->norm_gain)) return TRI_EALIGN;
+    Fusion fu{};
+    fu.gain = glue->norm ? reinterpret_cast<const uint16_t *>(glue->norm_gain) : nullptr;
+    fu.norm = glue->norm ? 1 : 0;
+    fu.eps = glue->norm_eps;
+    fu.pair = pair ? 1 : 0;
+    for (int g = 0; g < G; ++g) {
+        const _Float16 *r = glue->residual ? glue->residual[g] : nullptr;
+        if (pair && g == 1 && r) return TRI_EINVAL;
+        if (misaligned(r)) return TRI_EALIGN;
+        fu.res[g] = reinterpret_cast<const uint16_t *>(r);
+    }
+    int n[kMaxGroups];
+    uint16_t *y[kMaxGroups];
+    for (int g = 0; g < G; ++g) {
+        n[g] = (int)N[g];
+        y[g] = reinterpret_cast<uint16_t *>(Y[g]);
+    }
+    Groups gr = make_groups(G, Wp, scale, n, y);
+    if (pair) gr.blk[2] = gr.blk[1];            // the grid covers matrix 0's rows; each workgroup reads both
+    const uint16_t *x = reinterpret_cast<const uint16_t *>(X);
+    const bool done =
+        M == 1 ? launch_mv1(x, gr, (int)K, fmt, stream, &fu) : launch_mvm(x, gr, (int)M, (int)K, fmt, stream, &fu);
+    if (!done) return TRI_EINVAL;                // a shape the glue variants do not serve
+    return hipGetLastError() == hipSuccess ? TRI_OK : TRI_EHIP;
+}
+
 const char *tri_status_string(int code)
 {
     switch (code) {

@@ -22,6 +22,16 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
     return __builtin_amdgcn_fdot2(as_h2(a), as_h2(b), c, false);
 }
 
+// An fp16 bit pattern as fp32.
+__device__ __forceinline__ float h2f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
+// fp16_rne(a * b) lane by lane: one packed fp16 multiply (IEEE, round to nearest even; the
+// same result as rounding the exact fp32 product).
+__device__ __forceinline__ uint32_t mul2(uint32_t a, uint32_t b)
+{
+    return __builtin_bit_cast(uint32_t, as_h2(a) * as_h2(b));
+}
+
 // v_perm_b32: byte i of the result is byte sel_i of the 8-byte value {hi:lo}.
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
 {
@@ -109,6 +119,18 @@ __device__ __forceinline__ void swap16(float &a, float &b)
     const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
     a = __uint_as_float(r[0]);
     b = __uint_as_float(r[1]);
+}
+// v + (v of lane ^ 32) + (v of lane ^ 16) + (v of lane ^ 48): the sum over the four 16-lane
+// rows, in every lane.
+__device__ __forceinline__ float sum_over_rows(float v)
+{
+    float a = v, b = v;
+    swap32(a, b);
+    float s = a + b;
+    a = s;
+    b = s;
+    swap16(a, b);
+    return a + b;
 }
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v)

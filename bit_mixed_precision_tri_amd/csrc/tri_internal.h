@@ -50,6 +50,25 @@ inline Groups make_groups(int G, const uint8_t *const *Wp, const float *scale, c
     return gr;
 }
 
+// Glue of a decode block folded around a (grouped) layer in the small-M kernels.  The
+// residual (res[g] non-null: added to output g before rounding) is served by every variant;
+// the others are compile-time variants of the kernels (template bits kGlueNorm, kGluePair):
+//   norm: the activation rows are RMS-normalised, with an optional gain;
+//   pair: matrices 0 and 1 (same N) are the gate and up projections of a gated MLP, served by
+//         the same workgroups; only output 0 is written, fp16(silu(y0) * y1).
+struct Fusion {
+    const uint16_t *gain;                        // K fp16, or null (a gain of 1)
+    const uint16_t *res[kMaxGroups];             // M x N[g] fp16 per matrix, or null
+    float eps;
+    int norm;
+    int pair;
+};
+enum { kGlueNorm = 1, kGluePair = 2 };
+inline int glue_bits(const Fusion *fu)
+{
+    return fu ? (fu->norm ? kGlueNorm : 0) | (fu->pair ? kGluePair : 0) : 0;
+}
+
 // The matrix of a grouped launch that a workgroup (by its 16-row block) belongs to.
 __device__ __forceinline__ int group_of(const Groups &gr, int block)
 {
@@ -65,9 +84,10 @@ int launch_gemv2(const uint16_t *X, const uint8_t *Wp, float scale, int N, int K
 int launch_smallm(const uint16_t *X, const uint8_t *Wp, float scale, int M, int N, int K, int fmt, uint16_t *Y,
                   hipStream_t s);
 // M = 1 on MFMA (tri_mv1.hip) and 2 <= M <= 16 on MFMA (tri_mvm.hip), for one or several
-// matrices; false (nothing launched) if the shape is outside their range.
-bool launch_mv1(const uint16_t *X, const Groups &gr, int K, int fmt, hipStream_t s);
-bool launch_mvm(const uint16_t *X, const Groups &gr, int M, int K, int fmt, hipStream_t s);
+// matrices, with the block glue `fu` folded in when it is non-null; false (nothing launched)
+// if the shape is outside their range.
+bool launch_mv1(const uint16_t *X, const Groups &gr, int K, int fmt, hipStream_t s, const Fusion *fu = nullptr);
+bool launch_mvm(const uint16_t *X, const Groups &gr, int M, int K, int fmt, hipStream_t s, const Fusion *fu = nullptr);
 // The small-M kernels for one matrix: the two above, else the LDS-staged kernel for short rows;
 // false (nothing launched) if none of them takes the shape.
 bool launch_decode(const uint16_t *X, const uint8_t *Wp, float scale, int M, int N, int K, int fmt, uint16_t *Y,

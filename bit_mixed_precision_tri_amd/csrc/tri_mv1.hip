@@ -30,6 +30,13 @@
 // chunks with whole-line loads, permutes them into the A-operand order in LDS (no
 // workgroup barrier), and adds them up for sum_k x.  The waves' partial sums meet in LDS and
 // are added in a fixed order (no atomics).
+//
+// Block glue.  Every variant adds an optional residual to the fp32 result before rounding.
+// Norm variant (GL & kGlueNorm): the norm gain is read beside the activations; each lane adds
+// the squares of its activations (gathered like sum_k x), multiplies them by the gain
+// (rounded to fp16) and the 1/rms factor scales the result.  Pair variant (GL & kGluePair):
+// the workgroup also reads the same 16 rows of a second matrix, contracts them with the same
+// A operands, and writes fp16(silu(y0) * y1) -- the gated-MLP input -- as its only output.
 #include "tri_device.h"
 #include "tri_internal.h"
 
@@ -52,9 +59,12 @@ __device__ __forceinline__ float4_t mfma(const u32x4 a, const u32x4 b, float4_t 
 
 }  // namespace
 
-template <int FMT, int NW, int CST>
-__global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X, const Groups gr, int K, int C)
+template <int FMT, int NW, int CST, int GL>
+__global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X, const Groups gr, int K, int C,
+                                                 const Fusion fu)
 {
+    constexpr bool NORM = (GL & kGlueNorm) != 0;
+    constexpr bool PAIR = (GL & kGluePair) != 0;
     const int gi = group_of(gr, (int)blockIdx.x);
     const uint8_t *__restrict__ Wp = gr.Wp[gi];
     uint16_t *__restrict__ Y = gr.Y[gi];
@@ -71,7 +81,8 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
     __shared__ u32x4 xa[NW][NCH][NOP];           // per wave: A operands of its chunks
     __shared__ u32x4 xraw[TWO ? 1 : NW][TWO ? 1 : NCH * PIECES];   // 1.6-bit: raw pieces
     __shared__ uint32_t lut[TWO ? 1 : 256];
-    __shared__ float red[NW][17];
+    __shared__ float red[NW][NORM ? 18 : 17];    // per wave: the 16 rows, sum x (, sum x^2)
+    __shared__ float red1[PAIR ? NW : 1][16];    // pair: the second matrix's rows
 
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar descriptors)
@@ -88,28 +99,47 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
     //     4*((l/4)*NW + w) + l%4; piece P = 64i + lane of the wave's pieces is piece P % PIECES
     //     of local chunk P / PIECES, so a load instruction reads whole 128-byte lines
     const __amdgpu_buffer_rsrc_t xr = rsrc(X, (uint32_t)K * 2u);
-    u32x4 xv[NLD];
+    u32x4 xv[NLD], nv[NORM ? NLD : 1];
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
         const int P = 64 * i + lane;
         const int l = P / PIECES;
         const int gc = 4 * ((l >> 2) * NW + wv) + (l & 3);
         const int k = gc * XH + 8 * (P % PIECES);
-        xv[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)((l < NCH && k < K) ? (uint32_t)k * 2u : 0x80000000u),
-                                                      0, 0);
+        const int off = (l < NCH && k < K) ? (int)((uint32_t)k * 2u) : (int)0x80000000u;
+        xv[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
+        if constexpr (NORM) {                    // the norm gain of the same activations
+            if (fu.gain) nv[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc(fu.gain, (uint32_t)K * 2u), off, 0, 0);
+        }
     }
     // (2) every weight chunk of the wave, all in flight at once
     const int rows_here = min(16, N - n0);
     const __amdgpu_buffer_rsrc_t wr =
         rsrc(Wp + (int64_t)n0 * S, __builtin_amdgcn_readfirstlane((uint32_t)(rows_here * S)));
-    u32x4 wq[CST];
+    // (pair: the same chunks of the second matrix, requested in the order they are used)
+    const __amdgpu_buffer_rsrc_t wr1 =
+        rsrc(gr.Wp[PAIR ? 1 : 0] + (int64_t)n0 * S, __builtin_amdgcn_readfirstlane((uint32_t)(rows_here * S)));
+    u32x4 wq[CST], wq1[PAIR ? CST : 1];
 #pragma unroll
     for (int s = 0; s < CST; ++s) {
         const int c = 4 * (s * NW + wv) + g;
-        wq[s] = __builtin_amdgcn_raw_buffer_load_b128(wr, (int)(c < C ? (uint32_t)(j * S + c * 16) : 0x80000000u), 0, 0);
+        const int off = c < C ? (int)(uint32_t)(j * S + c * 16) : (int)0x80000000u;
+        wq[s] = __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 0);
+        if constexpr (PAIR) wq1[s] = __builtin_amdgcn_raw_buffer_load_b128(wr1, off, 0, 0);
     }
 
-    // (3) A operands in LDS, and this lane's share of sum_k x
+    // (3) norm: sum of squares, then x -> fp16(x * gain); A operands in LDS and this lane's
+    //     share of sum_k x
+    float xsq = 0.f;
+    if constexpr (NORM) {
+#pragma unroll
+        for (int i = 0; i < NLD; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                xsq = dot2(xv[i][e], xv[i][e], xsq);
+                if (fu.gain) xv[i][e] = mul2(xv[i][e], nv[i][e]);
+            }
+    }
     float xsum = 0.f;
 #pragma unroll
     for (int i = 0; i < NLD; ++i)
@@ -173,23 +203,18 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
 
     // (4) decode and contract, one MFMA per position (and half, 1.6-bit)
     const float4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-    float4_t acc[NCLS];
+    float4_t acc[NCLS], acc1[PAIR ? NCLS : 1];
 #pragma unroll
     for (int c = 0; c < NCLS; ++c) acc[c] = zero4;
 #pragma unroll
-    for (int s = 0; s < CST; ++s) {
-        if (4 * (s * NW + wv) >= C) break;       // wave-uniform: no chunk of this step is live
-        const u32x4 *asrc = &xa[wv][4 * s + g][0];
-        u32x4 a[NOP];
-#pragma unroll
-        for (int p = 0; p < NOP; ++p) a[p] = asrc[p];
-        const u32x4 v = wq[s];
+    for (int c = 0; c < (PAIR ? NCLS : 1); ++c) acc1[c] = zero4;
+    auto contract = [&](const u32x4 (&a)[NOP], const u32x4 v, float4_t (&ac)[NCLS]) __attribute__((always_inline)) {
         if constexpr (TWO) {
             const u32x4 u = v >> 12u;
 #pragma unroll
-            for (int p = 0; p < 6; ++p) acc[p] = mfma(a[p], v & (0x00030003u << (2 * p)), acc[p]);
-            acc[0] = mfma(a[6], u & 0x00030003u, acc[0]);
-            acc[1] = mfma(a[7], u & 0x000C000Cu, acc[1]);
+            for (int p = 0; p < 6; ++p) ac[p] = mfma(a[p], v & (0x00030003u << (2 * p)), ac[p]);
+            ac[0] = mfma(a[6], u & 0x00030003u, ac[0]);
+            ac[1] = mfma(a[7], u & 0x000C000Cu, ac[1]);
         } else {
             u32x4 lo, hi;
 #pragma unroll
@@ -202,22 +227,45 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
 #pragma unroll
             for (int p = 0; p < 5; ++p) {
                 const uint32_t m = 0x00030003u << (2 * p);
-                acc[p] = mfma(a[2 * p], lo & m, acc[p]);
-                acc[p] = mfma(a[2 * p + 1], hi & m, acc[p]);
+                ac[p] = mfma(a[2 * p], lo & m, ac[p]);
+                ac[p] = mfma(a[2 * p + 1], hi & m, ac[p]);
             }
         }
+    };
+#pragma unroll
+    for (int s = 0; s < CST; ++s) {
+        if (4 * (s * NW + wv) >= C) break;       // wave-uniform: no chunk of this step is live
+        const u32x4 *asrc = &xa[wv][4 * s + g][0];
+        u32x4 a[NOP];
+#pragma unroll
+        for (int p = 0; p < NOP; ++p) a[p] = asrc[p];
+        contract(a, wq[s], acc);
+        if constexpr (PAIR) contract(a, wq1[s], acc1);
     }
 
     // (5) merge classes (every row of a D tile is the same; row 0 is element 0 of lanes 0..15),
     //     add the waves' partial sums in a fixed order, subtract sum_k x, scale, round
+    auto merge = [&](const float4_t (&ac)[NCLS]) __attribute__((always_inline)) {
+        float4_t t = ac[0] + 0.25f * ac[1];
+        t += 0.0625f * ac[2] + 0.015625f * ac[3];
+        t += 0.00390625f * ac[4];
+        if constexpr (TWO) t += 0.0009765625f * ac[5];
+        return t;
+    };
     float xw[1] = {xsum};
     const float xs_wave = wave_reduce_rows<1>(xw, lane);
-    float4_t t = acc[0] + 0.25f * acc[1];
-    t += 0.0625f * acc[2] + 0.015625f * acc[3];
-    t += 0.00390625f * acc[4];
-    if constexpr (TWO) t += 0.0009765625f * acc[5];
+    const float4_t t = merge(acc);
     if (g == 0) red[wv][j] = t[0];
     if (lane == 0) red[wv][16] = xs_wave;
+    if constexpr (PAIR) {
+        const float4_t t1 = merge(acc1);
+        if (g == 0) red1[wv][j] = t1[0];
+    }
+    if constexpr (NORM) {
+        float xq[1] = {xsq};
+        const float xq_wave = wave_reduce_rows<1>(xq, lane);
+        if (lane == 0) red[wv][17] = xq_wave;
+    }
     __syncthreads();
     if (threadIdx.x < 16 && n0 + (int)threadIdx.x < N) {
         float sd = 0.f, sx = 0.f;
@@ -226,50 +274,85 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
             sd += red[w][threadIdx.x];
             sx += red[w][16];
         }
-        Y[n0 + threadIdx.x] = __builtin_bit_cast(uint16_t, (_Float16)((sd * 16777216.0f - sx) * scale));
+        float rinv = 1.f;
+        if constexpr (NORM) {
+            float sq = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) sq += red[w][17];
+            rinv = 1.f / sqrtf(sq / (float)K + fu.eps);
+        }
+        float y = (sd * 16777216.0f - sx) * scale * rinv;
+        if constexpr (PAIR) {
+            float sd1 = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) sd1 += red1[w][threadIdx.x];
+            const float y1 = (sd1 * 16777216.0f - sx) * gr.scale[1] * rinv;
+            y = y / (1.f + __expf(-y)) * y1;     // silu(gate) * up
+        }
+        if (fu.res[gi]) y += h2f(fu.res[gi][n0 + threadIdx.x]);
+        Y[n0 + threadIdx.x] = __builtin_bit_cast(uint16_t, (_Float16)y);
     }
 }
 
 template <int FMT, int NW, int CST>
-static void launch_cfg(const uint16_t *X, const Groups &gr, int K, int C, hipStream_t s)
+static void launch_cfg(const uint16_t *X, const Groups &gr, int K, int C, hipStream_t s, const Fusion *fu)
 {
-    hipLaunchKernelGGL((k_mv1<FMT, NW, CST>), dim3(gr.blk[gr.G]), dim3(64 * NW), 0, s, X, gr, K, C);
+    const Fusion f = fu ? *fu : Fusion{};
+    const dim3 grid(gr.blk[gr.G]), block(64 * NW);
+    const int gl = glue_bits(fu);
+    if constexpr (NW == 8) {                     // (pair variants: eight waves only, see launch_fmt)
+        if (gl == kGluePair) {
+            hipLaunchKernelGGL((k_mv1<FMT, NW, CST, kGluePair>), grid, block, 0, s, X, gr, K, C, f);
+            return;
+        }
+        if (gl == (kGlueNorm | kGluePair)) {
+            hipLaunchKernelGGL((k_mv1<FMT, NW, CST, kGlueNorm | kGluePair>), grid, block, 0, s, X, gr, K, C, f);
+            return;
+        }
+    }
+    if (gl & kGlueNorm)
+        hipLaunchKernelGGL((k_mv1<FMT, NW, CST, kGlueNorm>), grid, block, 0, s, X, gr, K, C, f);
+    else
+        hipLaunchKernelGGL((k_mv1<FMT, NW, CST, 0>), grid, block, 0, s, X, gr, K, C, f);
 }
 
 // Eight waves per 16 rows (measured best at K = 4096 and 11008); sixteen for long rows.
 template <int FMT>
-static bool launch_fmt(const uint16_t *X, const Groups &gr, int K, int C, hipStream_t s)
+static bool launch_fmt(const uint16_t *X, const Groups &gr, int K, int C, hipStream_t s, const Fusion *fu)
 {
     const int cst8 = (C + 31) / 32;              // chunk-steps with 8 waves (4 chunks per step and wave)
     switch (cst8) {
-    case 1: launch_cfg<FMT, 8, 1>(X, gr, K, C, s); return true;
-    case 2: launch_cfg<FMT, 8, 2>(X, gr, K, C, s); return true;
-    case 3: launch_cfg<FMT, 8, 3>(X, gr, K, C, s); return true;
-    case 4: launch_cfg<FMT, 8, 4>(X, gr, K, C, s); return true;
-    case 5: launch_cfg<FMT, 8, 5>(X, gr, K, C, s); return true;
-    case 6: launch_cfg<FMT, 8, 6>(X, gr, K, C, s); return true;
-    case 7: launch_cfg<FMT, 8, 7>(X, gr, K, C, s); return true;
-    case 8: launch_cfg<FMT, 8, 8>(X, gr, K, C, s); return true;
+    case 1: launch_cfg<FMT, 8, 1>(X, gr, K, C, s, fu); return true;
+    case 2: launch_cfg<FMT, 8, 2>(X, gr, K, C, s, fu); return true;
+    case 3: launch_cfg<FMT, 8, 3>(X, gr, K, C, s, fu); return true;
+    case 4: launch_cfg<FMT, 8, 4>(X, gr, K, C, s, fu); return true;
+    case 5: launch_cfg<FMT, 8, 5>(X, gr, K, C, s, fu); return true;
+    case 6: launch_cfg<FMT, 8, 6>(X, gr, K, C, s, fu); return true;
+    case 7: launch_cfg<FMT, 8, 7>(X, gr, K, C, s, fu); return true;
+    case 8: launch_cfg<FMT, 8, 8>(X, gr, K, C, s, fu); return true;
     default: break;
     }
-    // sixteen waves; the staged activations of a workgroup must fit in LDS
+    // sixteen waves; the staged activations of a workgroup must fit in LDS.  (The pair variant
+    // would exceed the registers a wave has at sixteen waves: longer rows are not paired.)
+    if (fu && fu->pair) return false;
     const int cst16 = (C + 63) / 64;
-    if (cst16 <= 6) { launch_cfg<FMT, 16, 6>(X, gr, K, C, s); return true; }
+    if (cst16 <= 6) { launch_cfg<FMT, 16, 6>(X, gr, K, C, s, fu); return true; }
     if constexpr (FMT == TRI_FMT_2BIT) {
-        if (cst16 <= 8) { launch_cfg<FMT, 16, 8>(X, gr, K, C, s); return true; }
-        if (cst16 <= 12) { launch_cfg<FMT, 16, 12>(X, gr, K, C, s); return true; }
+        if (cst16 <= 8) { launch_cfg<FMT, 16, 8>(X, gr, K, C, s, fu); return true; }
+        if (cst16 <= 12) { launch_cfg<FMT, 16, 12>(X, gr, K, C, s, fu); return true; }
     }
     return false;                                // longer rows: the streaming small-M kernel
 }
 
-bool launch_mv1(const uint16_t *X, const Groups &gr, int K, int fmt, hipStream_t s)
+bool launch_mv1(const uint16_t *X, const Groups &gr, int K, int fmt, hipStream_t s, const Fusion *fu)
 {
     const int C = (int)(row_bytes(K, fmt) / 16);
     // 32-bit buffer offsets: the activation row and one 16-row block stay below 2^31 bytes;
     // activations are read in pieces of 8 values, so K must be a multiple of 8
     if ((K % 8) != 0 || (int64_t)K * 2 >= ((int64_t)1 << 31) || 16 * (int64_t)C * 16 >= ((int64_t)1 << 31))
         return false;
-    return fmt == TRI_FMT_2BIT ? launch_fmt<TRI_FMT_2BIT>(X, gr, K, C, s) : launch_fmt<TRI_FMT_1P6BIT>(X, gr, K, C, s);
+    return fmt == TRI_FMT_2BIT ? launch_fmt<TRI_FMT_2BIT>(X, gr, K, C, s, fu)
+                             : launch_fmt<TRI_FMT_1P6BIT>(X, gr, K, C, s, fu);
 }
 
 }  // namespace tri

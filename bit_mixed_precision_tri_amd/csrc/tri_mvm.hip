@@ -17,6 +17,13 @@
 // through the wave's LDS slot to the lanes that use them, and permuted there into the
 // pairing of the decoded weights (2-bit: trits (16v+p, 16v+8+p); 1.6-bit: (5q+p, 5q+40+p)).
 // The waves' partial tiles are added in LDS in a fixed order (no atomics).
+//
+// Block glue.  Every variant adds an optional residual to the fp32 results before rounding.
+// Norm variant (GL & kGlueNorm): after the bounce each lane adds the squares of its row's
+// values and multiplies them by the norm gain (rounded to fp16), which travels as one more
+// row of the wave's LDS slot; the 1/rms factor of each row scales its results.  Pair variant
+// (GL & kGluePair): the workgroup also reads the same 16 rows of a second matrix, contracts
+// them with the same A operands, and writes fp16(silu(y0) * y1) as its only output.
 #include "tri_device.h"
 #include "tri_internal.h"
 
@@ -46,9 +53,12 @@ __device__ __forceinline__ void wave_sync()
 
 }  // namespace
 
-template <int FMT, int MT, int NW, int CST>
-__global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X, const Groups gr, int M, int K, int C)
+template <int FMT, int MT, int NW, int CST, int GL>
+__global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X, const Groups gr, int M, int K, int C,
+                                                 const Fusion fu)
 {
+    constexpr bool NORM = (GL & kGlueNorm) != 0;
+    constexpr bool PAIR = (GL & kGluePair) != 0;
     const int gi = group_of(gr, (int)blockIdx.x);
     const uint8_t *__restrict__ Wp = gr.Wp[gi];
     uint16_t *__restrict__ Y = gr.Y[gi];
@@ -61,9 +71,11 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
     constexpr int RP = 4 * XH / 8;               // 16-byte pieces of one row per step (32 or 40)
     constexpr int NLD = (MT * RP + 63) / 64;     // whole-line activation loads per lane and step
     constexpr int RPP = RP + 1;                  // padded row stride: the 16 rows a read touches fall in distinct banks
-    __shared__ u32x4 xraw[NW][MT * RPP];         // per wave: one step's activations, row-major
+    constexpr int XROWS = MT + (NORM ? 1 : 0);   // (+ the norm gain of the step's chunks)
+    __shared__ u32x4 xraw[NW][XROWS * RPP];      // per wave: one step's activations, row-major
     __shared__ uint32_t lut[TWO ? 1 : 256];
-    __shared__ float red[NW][16][17];            // per wave: partial tile [row m][column j], + sum x
+    __shared__ float red[NW][16][NORM ? 18 : 17];    // per wave: partial tile [row m][column j], + sum x (+ sum x^2)
+    __shared__ float red1[PAIR ? NW : 1][16][17];    // pair: the second matrix's partial tile
 
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar descriptors)
@@ -81,24 +93,38 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
     const int rows_here = min(16, N - n0);
     const __amdgpu_buffer_rsrc_t wr =
         rsrc(Wp + (int64_t)n0 * S, __builtin_amdgcn_readfirstlane((uint32_t)(rows_here * S)));
-    u32x4 wq[CST];
+    // (pair: the same chunks of the second matrix, requested in the order they are used)
+    const __amdgpu_buffer_rsrc_t wr1 =
+        rsrc(gr.Wp[PAIR ? 1 : 0] + (int64_t)n0 * S, __builtin_amdgcn_readfirstlane((uint32_t)(rows_here * S)));
+    u32x4 wq[CST], wq1[PAIR ? CST : 1];
 #pragma unroll
     for (int s = 0; s < CST; ++s) {
         const int c = 4 * (s * NW + wv) + g;
-        wq[s] = __builtin_amdgcn_raw_buffer_load_b128(wr, (int)(c < C ? (uint32_t)(j * S + c * 16) : 0x80000000u), 0, 0);
+        const int off = c < C ? (int)(uint32_t)(j * S + c * 16) : (int)0x80000000u;
+        wq[s] = __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 0);
+        if constexpr (PAIR) wq1[s] = __builtin_amdgcn_raw_buffer_load_b128(wr1, off, 0, 0);
     }
     // activations of step s: piece P = 64i + lane is piece P % RP of row P / RP, i.e. values
     // 16*(4*(s*NW + w)*XH/16 + P % RP) ... of that row: whole 128-byte lines per instruction
     const __amdgpu_buffer_rsrc_t xr = rsrc(X, __builtin_amdgcn_readfirstlane((uint32_t)((int64_t)M * K * 2)));
-    auto load_x = [&](int s, u32x4 (&xv)[NLD]) {
+    // (norm: and piece `lane` of the step's gain)
+    auto load_x = [&](int s, u32x4 (&xv)[NLD], u32x4 &nv) {
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
             const int P = 64 * i + lane;
             const int row = P / RP;
             const int k = 4 * (s * NW + wv) * XH + 8 * (P % RP);
             const bool live = row < M && k < K;
-            xv[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)(live ? (uint32_t)(row * K + k) * 2u : 0x80000000u),
-                                                          0, 0);
+            const int off = live ? (int)((uint32_t)(row * K + k) * 2u) : (int)0x80000000u;
+            xv[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
+        }
+        if constexpr (NORM) {
+            if (fu.gain) {
+                const int k = 4 * (s * NW + wv) * XH + 8 * lane;
+                nv = __builtin_amdgcn_raw_buffer_load_b128(
+                    rsrc(fu.gain, (uint32_t)K * 2u), (lane < RP && k < K) ? (int)((uint32_t)k * 2u) : (int)0x80000000u,
+                    0, 0);
+            }
         }
     };
 
@@ -106,27 +132,70 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
     float4_t acc[NCLS];
 #pragma unroll
     for (int c = 0; c < NCLS; ++c) acc[c] = zero4;
+    float4_t acc1[PAIR ? NCLS : 1];              // pair: the second matrix
+#pragma unroll
+    for (int c = 0; c < (PAIR ? NCLS : 1); ++c) acc1[c] = zero4;
+    auto contract = [&](const u32x4 (&a)[NOP], const u32x4 v, float4_t (&ac)[NCLS]) __attribute__((always_inline)) {
+        if constexpr (TWO) {
+            const u32x4 u = v >> 12u;
+#pragma unroll
+            for (int p = 0; p < 6; ++p) ac[p] = mfma(a[p], v & (0x00030003u << (2 * p)), ac[p]);
+            ac[0] = mfma(a[6], u & 0x00030003u, ac[0]);
+            ac[1] = mfma(a[7], u & 0x000C000Cu, ac[1]);
+        } else {
+            u32x4 lo, hi;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const uint32_t blo = (v[q >> 2] >> (8 * (q & 3))) & 0xFFu;
+                const uint32_t bhi = (v[2 + (q >> 2)] >> (8 * (q & 3))) & 0xFFu;
+                const uint32_t pq = lut[blo] | (lut[bhi] << 16);
+                if (q < 4) lo[q] = pq; else hi[q - 4] = pq;
+            }
+#pragma unroll
+            for (int p = 0; p < 5; ++p) {
+                const uint32_t m = 0x00030003u << (2 * p);
+                ac[p] = mfma(a[2 * p], lo & m, ac[p]);
+                ac[p] = mfma(a[2 * p + 1], hi & m, ac[p]);
+            }
+        }
+    };
     float4_t accx = zero4;                       // sum_k X[m][k] in every column of the tile
+    float xsq = 0.f;                             // norm: sum of x^2 over this lane's values of row j
     // the activations of PD steps are in flight at once (a ring of register sets; one step
     // ahead measured best: deeper rings gained nothing)
     constexpr int PD = 1;
-    u32x4 xv[PD][NLD];
+    u32x4 xv[PD][NLD], nv[PD];
 #pragma unroll
-    for (int t = 0; t < PD; ++t) load_x(t, xv[t]);
+    for (int t = 0; t < PD; ++t) load_x(t, xv[t], nv[t]);
 #pragma unroll
     for (int s = 0; s < CST; ++s) {
         if (4 * (s * NW + wv) >= C) break;       // wave-uniform: no chunk of this step is live
         // bounce the step's raw activations to the lanes that use them, then permute there
+        if constexpr (NORM) {
+            if (fu.gain && lane < RP) xraw[wv][MT * RPP + lane] = nv[s % PD];
+        }
 #pragma unroll
         for (int i = 0; i < NLD; ++i)
             if (64 * i + lane < MT * RP) xraw[wv][64 * i + lane + (64 * i + lane) / RP] = xv[s % PD][i];
         wave_sync();
-        if (s + PD < CST) load_x(s + PD, xv[s % PD]);   // refill the set just emptied
+        if (s + PD < CST) load_x(s + PD, xv[s % PD], nv[s % PD]);   // refill the set just emptied
         uint32_t x32[XH / 2];                    // row j, chunk g of the step (zero past the tile's rows)
 #pragma unroll
         for (int q = 0; q < XH / 8; ++q) {
             const u32x4 v = j < MT ? xraw[wv][j * RPP + (XH / 8) * g + q] : u32x4{0u, 0u, 0u, 0u};
             x32[4 * q] = v[0]; x32[4 * q + 1] = v[1]; x32[4 * q + 2] = v[2]; x32[4 * q + 3] = v[3];
+        }
+        if constexpr (NORM) {
+#pragma unroll
+            for (int q = 0; q < XH / 2; ++q) xsq = dot2(x32[q], x32[q], xsq);
+            if (fu.gain) {
+#pragma unroll
+                for (int q = 0; q < XH / 8; ++q) {
+                    const u32x4 gq = xraw[wv][MT * RPP + (XH / 8) * g + q];   // the same for every row
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x32[4 * q + e] = mul2(x32[4 * q + e], gq[e]);
+                }
+            }
         }
         wave_sync();                             // the slot may be refilled at the next step
         u32x4 a[NOP];
@@ -154,41 +223,33 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
 #pragma unroll
         for (int p = 0; p < NOP; ++p) accx = mfma(a[p], ones, accx);
         // decode and contract
-        const u32x4 v = wq[s];
-        if constexpr (TWO) {
-            const u32x4 u = v >> 12u;
-#pragma unroll
-            for (int p = 0; p < 6; ++p) acc[p] = mfma(a[p], v & (0x00030003u << (2 * p)), acc[p]);
-            acc[0] = mfma(a[6], u & 0x00030003u, acc[0]);
-            acc[1] = mfma(a[7], u & 0x000C000Cu, acc[1]);
-        } else {
-            u32x4 lo, hi;
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const uint32_t blo = (v[q >> 2] >> (8 * (q & 3))) & 0xFFu;
-                const uint32_t bhi = (v[2 + (q >> 2)] >> (8 * (q & 3))) & 0xFFu;
-                const uint32_t pq = lut[blo] | (lut[bhi] << 16);
-                if (q < 4) lo[q] = pq; else hi[q - 4] = pq;
-            }
-#pragma unroll
-            for (int p = 0; p < 5; ++p) {
-                const uint32_t m = 0x00030003u << (2 * p);
-                acc[p] = mfma(a[2 * p], lo & m, acc[p]);
-                acc[p] = mfma(a[2 * p + 1], hi & m, acc[p]);
-            }
-        }
+        contract(a, wq[s], acc);
+        if constexpr (PAIR) contract(a, wq1[s], acc1);
     }
 
     // merge classes: lane (g, j) holds rows 4g + e of column j (of D and of the sums of X)
-    float4_t t = acc[0] + 0.25f * acc[1];
-    t += 0.0625f * acc[2] + 0.015625f * acc[3];
-    t += 0.00390625f * acc[4];
-    if constexpr (TWO) t += 0.0009765625f * acc[5];
+    auto merge = [&](const float4_t (&ac)[NCLS]) __attribute__((always_inline)) {
+        float4_t t = ac[0] + 0.25f * ac[1];
+        t += 0.0625f * ac[2] + 0.015625f * ac[3];
+        t += 0.00390625f * ac[4];
+        if constexpr (TWO) t += 0.0009765625f * ac[5];
+        return t;
+    };
+    const float4_t t = merge(acc);
 #pragma unroll
     for (int e = 0; e < 4; ++e) red[wv][4 * g + e][j] = t[e];
     if (j == 0) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) red[wv][4 * g + e][16] = accx[e];
+    }
+    if constexpr (PAIR) {
+        const float4_t t1 = merge(acc1);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red1[wv][4 * g + e][j] = t1[e];
+    }
+    if constexpr (NORM) {
+        const float q = sum_over_rows(xsq);      // lanes j, j+16, j+32, j+48 hold parts of row j
+        if (g == 0) red[wv][j][17] = q;
     }
     __syncthreads();
     // thread (m, jj): output Y[m][n0 + jj], waves added in a fixed order
@@ -201,42 +262,90 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
                 sd += red[w][m][jj];
                 sx += red[w][m][16];
             }
-            Y[(int64_t)m * N + n0 + jj] = __builtin_bit_cast(uint16_t, (_Float16)((sd * 16777216.0f - sx) * scale));
+            float rinv = 1.f;
+            if constexpr (NORM) {
+                float sq = 0.f;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) sq += red[w][m][17];
+                rinv = 1.f / sqrtf(sq / (float)K + fu.eps);
+            }
+            float y = (sd * 16777216.0f - sx) * scale * rinv;
+            if constexpr (PAIR) {
+                float sd1 = 0.f;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) sd1 += red1[w][m][jj];
+                const float y1 = (sd1 * 16777216.0f - sx) * gr.scale[1] * rinv;
+                y = y / (1.f + __expf(-y)) * y1; // silu(gate) * up
+            }
+            if (fu.res[gi]) y += h2f(fu.res[gi][(int64_t)m * N + n0 + jj]);
+            Y[(int64_t)m * N + n0 + jj] = __builtin_bit_cast(uint16_t, (_Float16)y);
         }
     }
 }
 
-template <int FMT, int MT, int NW, int CST>
-static void launch_cfg(const uint16_t *X, const Groups &gr, int M, int K, int C, hipStream_t s)
+// Glue variants that exist: eight waves only (the slots of sixteen, one row longer, overflow
+// LDS), and none whose registers would overflow (1.6-bit tiles of 16 rows past 6 steps; pairs
+// of 16-row tiles past 4 steps).
+template <int FMT, int MT, int NW, int CST, int GL>
+constexpr bool has_glue()
 {
-    hipLaunchKernelGGL((k_mvm<FMT, MT, NW, CST>), dim3(gr.blk[gr.G]), dim3(64 * NW), 0, s, X, gr, M, K, C);
+    if (GL == 0) return true;
+    if (NW != 8) return false;
+    if ((GL & kGlueNorm) && FMT == TRI_FMT_1P6BIT && MT == 16 && CST > 6) return false;
+    if ((GL & kGluePair) && MT == 16 && CST > 4) return false;
+    return true;
+}
+
+template <int FMT, int MT, int NW, int CST, int GL>
+static bool launch_gl(const uint16_t *X, const Groups &gr, int M, int K, int C, hipStream_t s, const Fusion &f)
+{
+    if constexpr (has_glue<FMT, MT, NW, CST, GL>()) {
+        hipLaunchKernelGGL((k_mvm<FMT, MT, NW, CST, GL>), dim3(gr.blk[gr.G]), dim3(64 * NW), 0, s, X, gr, M, K, C, f);
+        return true;
+    }
+    return false;
+}
+
+template <int FMT, int MT, int NW, int CST>
+static bool launch_cfg(const uint16_t *X, const Groups &gr, int M, int K, int C, hipStream_t s, const Fusion *fu)
+{
+    const Fusion f = fu ? *fu : Fusion{};
+    switch (glue_bits(fu)) {
+    case kGlueNorm: return launch_gl<FMT, MT, NW, CST, kGlueNorm>(X, gr, M, K, C, s, f);
+    case kGluePair: return launch_gl<FMT, MT, NW, CST, kGluePair>(X, gr, M, K, C, s, f);
+    case kGlueNorm | kGluePair: return launch_gl<FMT, MT, NW, CST, kGlueNorm | kGluePair>(X, gr, M, K, C, s, f);
+    default: return launch_gl<FMT, MT, NW, CST, 0>(X, gr, M, K, C, s, f);
+    }
 }
 
 template <int FMT, int MT>
-static bool launch_mt(const uint16_t *X, const Groups &gr, int M, int K, int C, hipStream_t s)
+static bool launch_mt(const uint16_t *X, const Groups &gr, int M, int K, int C, hipStream_t s,
+                      const Fusion *fu)
 {
     const int cst8 = (C + 31) / 32;              // chunk-steps with 8 waves (4 chunks per step and wave)
     switch (cst8) {
-    case 1: launch_cfg<FMT, MT, 8, 1>(X, gr, M, K, C, s); return true;
-    case 2: launch_cfg<FMT, MT, 8, 2>(X, gr, M, K, C, s); return true;
-    case 3: launch_cfg<FMT, MT, 8, 3>(X, gr, M, K, C, s); return true;
-    case 4: launch_cfg<FMT, MT, 8, 4>(X, gr, M, K, C, s); return true;
-    case 5: launch_cfg<FMT, MT, 8, 5>(X, gr, M, K, C, s); return true;
-    case 6: launch_cfg<FMT, MT, 8, 6>(X, gr, M, K, C, s); return true;
-    case 7: launch_cfg<FMT, MT, 8, 7>(X, gr, M, K, C, s); return true;
-    case 8: launch_cfg<FMT, MT, 8, 8>(X, gr, M, K, C, s); return true;
+    case 1: return launch_cfg<FMT, MT, 8, 1>(X, gr, M, K, C, s, fu);
+    case 2: return launch_cfg<FMT, MT, 8, 2>(X, gr, M, K, C, s, fu);
+    case 3: return launch_cfg<FMT, MT, 8, 3>(X, gr, M, K, C, s, fu);
+    case 4: return launch_cfg<FMT, MT, 8, 4>(X, gr, M, K, C, s, fu);
+    case 5: return launch_cfg<FMT, MT, 8, 5>(X, gr, M, K, C, s, fu);
+    case 6: return launch_cfg<FMT, MT, 8, 6>(X, gr, M, K, C, s, fu);
+    case 7: return launch_cfg<FMT, MT, 8, 7>(X, gr, M, K, C, s, fu);
+    case 8: return launch_cfg<FMT, MT, 8, 8>(X, gr, M, K, C, s, fu);
     default: break;
     }
-    // sixteen waves, while the per-wave activation slots fit in LDS
+    // sixteen waves, while the per-wave activation slots fit in LDS (the norm and pair variants
+    // stay at eight waves)
+    if (glue_bits(fu)) return false;
     if constexpr (FMT == TRI_FMT_2BIT || MT <= 8) {
         const int cst16 = (C + 63) / 64;
-        if (cst16 <= 8) { launch_cfg<FMT, MT, 16, 8>(X, gr, M, K, C, s); return true; }
-        if (cst16 <= 16) { launch_cfg<FMT, MT, 16, 16>(X, gr, M, K, C, s); return true; }
+        if (cst16 <= 8) return launch_cfg<FMT, MT, 16, 8>(X, gr, M, K, C, s, fu);
+        if (cst16 <= 16) return launch_cfg<FMT, MT, 16, 16>(X, gr, M, K, C, s, fu);
     }
     return false;                                // longer rows: the streaming small-M kernel
 }
 
-bool launch_mvm(const uint16_t *X, const Groups &gr, int M, int K, int fmt, hipStream_t s)
+bool launch_mvm(const uint16_t *X, const Groups &gr, int M, int K, int fmt, hipStream_t s, const Fusion *fu)
 {
     const int C = (int)(row_bytes(K, fmt) / 16);
     // 32-bit buffer offsets: the activations and one 16-row block stay below 2^31 bytes;
@@ -244,10 +353,14 @@ bool launch_mvm(const uint16_t *X, const Groups &gr, int M, int K, int fmt, hipS
     if (M < 2 || M > 16 || (K % 8) != 0 || (int64_t)M * K * 2 >= ((int64_t)1 << 31) ||
         16 * (int64_t)C * 16 >= ((int64_t)1 << 31))
         return false;
-    const bool two = fmt == TRI_FMT_2BIT;
-    if (M <= 4) return two ? launch_mt<TRI_FMT_2BIT, 4>(X, gr, M, K, C, s) : launch_mt<TRI_FMT_1P6BIT, 4>(X, gr, M, K, C, s);
-    if (M <= 8) return two ? launch_mt<TRI_FMT_2BIT, 8>(X, gr, M, K, C, s) : launch_mt<TRI_FMT_1P6BIT, 8>(X, gr, M, K, C, s);
-    return two ? launch_mt<TRI_FMT_2BIT, 16>(X, gr, M, K, C, s) : launch_mt<TRI_FMT_1P6BIT, 16>(X, gr, M, K, C, s);
+    if (fmt == TRI_FMT_2BIT) {
+        if (M <= 4) return launch_mt<TRI_FMT_2BIT, 4>(X, gr, M, K, C, s, fu);
+        if (M <= 8) return launch_mt<TRI_FMT_2BIT, 8>(X, gr, M, K, C, s, fu);
+        return launch_mt<TRI_FMT_2BIT, 16>(X, gr, M, K, C, s, fu);
+    }
+    if (M <= 4) return launch_mt<TRI_FMT_1P6BIT, 4>(X, gr, M, K, C, s, fu);
+    if (M <= 8) return launch_mt<TRI_FMT_1P6BIT, 8>(X, gr, M, K, C, s, fu);
+    return launch_mt<TRI_FMT_1P6BIT, 16>(X, gr, M, K, C, s, fu);
 }
 
 }  // namespace tri

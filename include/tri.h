@@ -139,6 +139,43 @@ int tri_linear_grouped(const _Float16 *X, const uint8_t *const *Wp, const float 
                        const int64_t *N, int64_t K, int fmt, _Float16 *const *Y, int G,
                        hipStream_t stream);
 
+/* The glue of a decode block folded into a grouped layer (tri_linear_fused).  The
+ * pages name the parts of a block, not this placement (Pith review, "If this is
+ * right": the end-to-end speed-up trails the layer's because of the work outside
+ * the linear layers). */
+typedef struct {
+    const _Float16 *norm_gain;         /* K fp16, or NULL for a gain of 1 */
+    int norm;                          /* non-zero: RMS-normalise each input row:
+                                          x * gain / sqrt(mean_k(x^2) + norm_eps) */
+    float norm_eps;                    /* >= 0 and finite */
+    int pair;                          /* non-zero: G == 2 and N[0] == N[1]; matrices 0 and 1
+                                          are the gate and up projections of a gated MLP and
+                                          only Y[0] = fp16(silu(y0) * y1) is written, with
+                                          silu(z) = z / (1 + e^-z) (Y[1] may be NULL) */
+    const _Float16 *const *residual;   /* NULL, or a HOST array of G pointers, each NULL or an
+                                          M*N[g] fp16 residual added before rounding (it may
+                                          be Y[g] itself: an in-place residual add); with
+                                          pair, residual[1] must be NULL */
+} tri_glue;
+
+/* tri_linear_grouped with the glue: for g < G (g = 0 only with pair),
+ *   y_g  = scale[g] * (x' W_g^T),  x' = rmsnorm(X) if norm, else X;
+ *   Y[g] = fp16_rne( residual[g] + (pair ? silu(y_0) * y_1 : y_g) ).
+ * The y_g are fp32 (never rounded on their own); the gained activations are
+ * rounded to fp16 as an unfused RMSNorm output would be.  Served by the small-M
+ * kernels in one launch for all G matrices; needs M <= 16 and K % 8 == 0.  With
+ * norm or pair, K <= 16384 (2-bit) or K <= 20480 (1.6-bit), and for M > 8 also
+ * K <= 15360 (1.6-bit with norm) and K <= 8192 / 10240 (2-bit / 1.6-bit with
+ * pair); with neither, the row limits of tri_linear's MFMA small-M kernels apply
+ * (K <= 16384 / 20480 at least).  Other shapes are rejected with TRI_EINVAL
+ * before anything is launched.  norm_gain and the residuals must be 16-byte aligned
+ * device pointers and must not alias Wp or (except residual[g] == Y[g]) any Y.
+ * Errors: those of tri_linear_grouped, TRI_EINVAL for a null glue, a bad eps, a
+ * bad pair or a shape outside the range above, TRI_EALIGN. */
+int tri_linear_fused(const _Float16 *X, const uint8_t *const *Wp, const float *scale, int64_t M,
+                     const int64_t *N, int64_t K, int fmt, _Float16 *const *Y, int G,
+                     const tri_glue *glue, hipStream_t stream);
+
 /* The algorithm tri_linear would pick for (M, N, K, fmt); TRI_EINVAL if invalid. */
 int tri_select_algo(int64_t M, int64_t N, int64_t K, int fmt);
 

@@ -148,3 +148,37 @@ def test_quantize_workspace_and_argument_errors_launch_nothing():
     assert raw("tri_quantize", A, 4, 64, F2, ODD, C, A, need, s) == tri.TRI_EALIGN
     assert raw("tri_quantize", A, 4, 64, F2, B, C + 2, A, need, s) == tri.TRI_EALIGN
     assert raw("tri_quantize", A, 4, 64, F2, B, C, ODD, need, s) == tri.TRI_EALIGN
+
+
+def test_fused_argument_errors_launch_nothing():
+    import ctypes
+    F2 = tri.TRI_FMT_2BIT
+    s = None
+    ptrs = lambda *v: (ctypes.c_void_p * len(v))(*v)
+    floats = lambda *v: (ctypes.c_float * len(v))(*v)
+    ints = lambda *v: (ctypes.c_int64 * len(v))(*v)
+    wp, sc, nn, yy = ptrs(B, B), floats(1.0, 1.0), ints(4, 8), ptrs(C, C)
+    glue = lambda gain=None, norm=1, eps=1e-5, pair=0, res=None: ctypes.byref(tri.TriGlue(gain, norm, eps, pair, res))
+    g = glue()
+    call = lambda *a: raw("tri_linear_fused", *a)
+    assert call(A, wp, sc, 1, nn, 64, F2, yy, 2, None, s) == tri.TRI_EINVAL     # no glue
+    assert call(A, wp, sc, 1, nn, 64, F2, yy, 0, g, s) == tri.TRI_EINVAL
+    assert call(A, wp, sc, 17, nn, 64, F2, yy, 2, g, s) == tri.TRI_EINVAL       # M > 16
+    assert call(A, wp, sc, 1, nn, 60, F2, yy, 2, g, s) == tri.TRI_EINVAL        # K % 8
+    assert call(A, wp, sc, 1, nn, 16392, F2, yy, 2, g, s) == tri.TRI_EINVAL     # rows too long for the norm
+    n44 = ints(4, 4)
+    assert call(A, wp, sc, 16, n44, 8200, F2, yy, 2, glue(norm=0, pair=1), s) == tri.TRI_EINVAL   # pair, M > 8
+    for eps in (-1.0, float("nan"), float("inf")):
+        assert call(A, wp, sc, 1, nn, 64, F2, yy, 2, glue(eps=eps), s) == tri.TRI_EINVAL
+    # pair: two matrices of the same N, no residual on the second
+    assert call(A, wp, sc, 1, nn, 64, F2, yy, 2, glue(pair=1), s) == tri.TRI_EINVAL            # N differ
+    assert call(A, ptrs(B, B, B), floats(1, 1, 1), 1, ints(4, 4, 4), 64, F2, ptrs(C, C, C), 3,
+                glue(pair=1), s) == tri.TRI_EINVAL
+    res2 = ctypes.cast(ptrs(None, C), ctypes.c_void_p).value
+    assert call(A, wp, sc, 1, n44, 64, F2, yy, 2, glue(pair=1, res=res2), s) == tri.TRI_EINVAL
+    # alignment
+    assert call(A, wp, sc, 1, nn, 64, F2, yy, 2, glue(gain=ODD), s) == tri.TRI_EALIGN
+    resodd = ctypes.cast(ptrs(None, ODD), ctypes.c_void_p).value
+    assert call(A, wp, sc, 1, nn, 64, F2, yy, 2, glue(norm=0, res=resodd), s) == tri.TRI_EALIGN
+    assert call(ODD, wp, sc, 1, nn, 64, F2, yy, 2, g, s) == tri.TRI_EALIGN
+    assert call(A, wp, sc, 1, ints(4, 0), 64, F2, yy, 2, g, s) == tri.TRI_EINVAL

@@ -231,7 +231,9 @@ def test_batched_decode_full_size(fmt):
 
 @pytest.mark.parametrize("M", configs.BLOCK["Ms"])
 def test_block_step(M):
-    """Seven chained linears of one decode block; every linear is checked on its actual input."""
+    """Seven chained linears of one decode block with the glue on the CPU: every GPU linear is
+    checked on the input the oracle chain gives it, and the GPU chain's output against the
+    oracle chain's."""
     cfg = configs.BLOCK
     layers = {}
     for li, (name, K, N) in enumerate(cfg["layers"]):
@@ -242,17 +244,18 @@ def test_block_step(M):
 
     def gpu_linear(name, a):
         W, Wp, s, K = layers[name]
-        Y = run_layer(a, Wp, s, K, cfg["fmt"], tri.TRI_ALGO_AUTO)
-        check_layer(Y, a, W, s, "block M=%d layer %s" % (M, name))
-        return Y
+        return run_layer(a, Wp, s, K, cfg["fmt"], tri.TRI_ALGO_AUTO)
 
     def ref_linear(name, a):
         W, _, s, _ = layers[name]
         return oracle.linear_f64(a, W, s).astype(np.float16)
 
     say("block step M=%d" % M)
+    out_ref, ins_ref = block_glue.block_step(x0, ref_linear)
+    for name, a in ins_ref.items():
+        W, _, s, _ = layers[name]
+        check_layer(gpu_linear(name, a), a, W, s, "block M=%d layer %s" % (M, name))
     out_gpu, _ = block_glue.block_step(x0, gpu_linear)
-    out_ref, _ = block_glue.block_step(x0, ref_linear)
     rel = np.linalg.norm(out_gpu - out_ref) / np.linalg.norm(out_ref)
     say("  block output relative difference GPU chain vs oracle chain: %.3g" % rel)
     assert rel < 1e-2
