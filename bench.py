@@ -291,6 +291,7 @@ def main():
         "read_floor": floors,
     }
     if not args.skip_extra:
+        out["decode_1p6bit"] = bench_decode_1p6(clock)
         out["batched"] = bench_batched(clock)
         out["block"] = bench_block(clock)
         out["prefill"] = bench_prefill(clock)
@@ -314,6 +315,28 @@ def bench_batched(clock):
                             "GBps": round(L.bytes / t / 1e9, 1), "frac_hbm": round(L.bytes / t / 1e9 / HBM_PEAK_GBS, 4)})
                 del L
                 torch.cuda.empty_cache()
+    return res
+
+
+def bench_decode_1p6(clock):
+    """The decode shapes at M = 1 with 1.6-bit packed weights (k_mv1, base-3 digits through the LDS
+    byte table), cold weights; with the size-matched read floor of the 1.6-bit bytes."""
+    import torch
+    import bit_mixed_precision_tri_amd as tri
+    from bit_mixed_precision_tri_amd import configs
+    dcfg = configs.DECODE
+    F16 = tri.TRI_FMT_1P6BIT
+    res = []
+    for li, (name, K, N) in enumerate(dcfg["shapes"]):
+        L = Layer(dcfg["workload_id"], 20 + li, 1, N, K, F16)
+        t, _ = clock.run([L.launch] * 200)
+        nb = N * tri.tri_row_bytes(K, F16)
+        del L
+        torch.cuda.empty_cache()
+        tf = read_floor(nb, clock)
+        res.append({"shape": name, "K": K, "N": N, "bytes": effective_bytes(1, N, K, F16),
+                    "kernel_us": round(t * 1e6, 3), "GBps": round(effective_bytes(1, N, K, F16) / t / 1e9, 1),
+                    "read_floor_us": round(tf * 1e6, 3)})
     return res
 
 
