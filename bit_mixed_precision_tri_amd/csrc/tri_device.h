@@ -78,6 +78,34 @@ __device__ __forceinline__ uint32_t base3_digits_2bit(uint32_t b)
     return code;
 }
 
+// Base-3 digits of two bytes at once, for the 1.6-bit packing ("Spectra 1.1", Pith review,
+// "Referee Report" minor comment 5: the decode is the repeated division b'_i -> x_i).  `b`
+// holds one byte value per 16-bit lane; digit j of both is returned in d[j], one per lane:
+// d[j] = q_j - 3 q_{j+1} with q_j = floor(b / 3^j), each quotient an exact multiply-shift
+// (b*171 >> 9, b*57 >> 9, b*19 >> 9, b*203 >> 14; exact and below 2^16 for every b < 256).
+// A lane's digit read as fp16 bits is the exact value d * 2^-24.
+__device__ __forceinline__ void base3_digits_u16x2(uint32_t b, uint32_t (&d)[5])
+{
+    typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+    const u16x2 v = __builtin_bit_cast(u16x2, b);
+    const u16x2 q1 = (v * (uint16_t)171) >> (uint16_t)9;
+    const u16x2 q2 = (v * (uint16_t)57) >> (uint16_t)9;
+    const u16x2 q3 = (v * (uint16_t)19) >> (uint16_t)9;
+    const u16x2 q4 = (v * (uint16_t)203) >> (uint16_t)14;
+    d[0] = __builtin_bit_cast(uint32_t, (u16x2)(v - q1 * (uint16_t)3));
+    d[1] = __builtin_bit_cast(uint32_t, (u16x2)(q1 - q2 * (uint16_t)3));
+    d[2] = __builtin_bit_cast(uint32_t, (u16x2)(q2 - q3 * (uint16_t)3));
+    d[3] = __builtin_bit_cast(uint32_t, (u16x2)(q3 - q4 * (uint16_t)3));
+    d[4] = __builtin_bit_cast(uint32_t, q4);
+}
+
+// Bytes q and q + 8 (q < 8) of a 16-byte chunk as the two 16-bit lanes of one register.
+__device__ __forceinline__ uint32_t byte_pair(const u32x4 v, int q)
+{
+    const uint32_t sel = (uint32_t)(q & 3) | 0x0C00u | ((uint32_t)(4 + (q & 3)) << 16) | 0x0C000000u;
+    return perm(v[2 + (q >> 2)], v[q >> 2], sel);
+}
+
 // 16-byte global load.
 __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
 

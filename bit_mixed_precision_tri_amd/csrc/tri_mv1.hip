@@ -17,10 +17,11 @@
 // sum_k d*x; since t = d - 1, sum_k x is subtracted once per row at the end.
 //   2-bit:   a register pairs trits (16v+p, 16v+8+p); positions 6, 7 are taken from the
 //            word shifted right by 12, so they share the classes of 0 and 1.
-//   1.6-bit: each byte goes through a 256-entry LDS table to its five base-3 digits at bits
-//            2j (the repeated division b'_i -> x_i that the review's referee report
-//            describes for the paper's section 3.2), and bytes q and q+8 of a chunk share a
-//            register: position p pairs trits (5q+p, 5q+40+p).
+//   1.6-bit: bytes q and q+8 of a chunk become the two 16-bit lanes of a register, whose five
+//            base-3 digits (the repeated division b'_i -> x_i that the review's referee report
+//            describes for the paper's section 3.2) come from exact multiply-shift quotients,
+//            one digit per lane and register: position p pairs trits (5q+p, 5q+40+p), and every
+//            digit reads as d * 2^-24, so the two halves of a chunk need one accumulator each.
 // The sum over k is order-free, so the activations are permuted into the same pairing.
 //
 // Work split.  A workgroup of NW waves owns 16 weight rows; wave w takes chunk-steps s,
@@ -73,14 +74,13 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
     constexpr bool TWO = FMT == TRI_FMT_2BIT;
     constexpr int XH = TWO ? 64 : 80;            // activations per chunk
     constexpr int NOP = TWO ? 8 : 10;            // A operands (MFMAs) per chunk
-    constexpr int NCLS = TWO ? 6 : 5;            // position classes
+    constexpr int NCLS = TWO ? 6 : 2;            // accumulators: position classes (2-bit), halves (1.6-bit)
     constexpr int NCH = 4 * CST;                 // chunks per wave
     constexpr int PIECES = XH / 8;               // 16-byte activation pieces per chunk
     constexpr int NLD = (NCH * PIECES + 63) / 64;   // whole-line activation loads per lane
     static_assert(NCH <= 64, "chunks per wave");
     __shared__ u32x4 xa[NW][NCH][NOP];           // per wave: A operands of its chunks
     __shared__ u32x4 xraw[TWO ? 1 : NW][TWO ? 1 : NCH * PIECES];   // 1.6-bit: raw pieces
-    __shared__ uint32_t lut[TWO ? 1 : 256];
     __shared__ float red[NW][NORM ? 18 : 17];    // per wave: the 16 rows, sum x (, sum x^2)
     __shared__ float red1[PAIR ? NW : 1][16];    // pair: the second matrix's rows
 
@@ -90,10 +90,6 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
     const int j = lane & 15;
     const int n0 = ((int)blockIdx.x - gr.blk[gi]) * 16;
     const int64_t S = (int64_t)C * 16;
-
-    if constexpr (!TWO) {
-        for (int b = threadIdx.x; b < 256; b += 64 * NW) lut[b] = base3_digits_2bit((uint32_t)b);
-    }
 
     // (1) activations of this wave's chunks: local chunk l is global chunk
     //     4*((l/4)*NW + w) + l%4; piece P = 64i + lane of the wave's pieces is piece P % PIECES
@@ -195,7 +191,6 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
                     xa[wv][lane][2 * p + hh] = a;
                 }
         }
-        __syncthreads();                          // the byte table is shared by the workgroup
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -216,19 +211,15 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
             ac[0] = mfma(a[6], u & 0x00030003u, ac[0]);
             ac[1] = mfma(a[7], u & 0x000C000Cu, ac[1]);
         } else {
-            u32x4 lo, hi;
+            // register q: bytes q and q+8, position p pairs trits (5q+p, 5q+40+p); every digit
+            // carries the same scale, so the halves accumulate in ac[0] and ac[1]
+            uint32_t dg[8][5];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const uint32_t blo = (v[q >> 2] >> (8 * (q & 3))) & 0xFFu;
-                const uint32_t bhi = (v[2 + (q >> 2)] >> (8 * (q & 3))) & 0xFFu;
-                const uint32_t pq = lut[blo] | (lut[bhi] << 16);
-                if (q < 4) lo[q] = pq; else hi[q - 4] = pq;
-            }
+            for (int q = 0; q < 8; ++q) base3_digits_u16x2(byte_pair(v, q), dg[q]);
 #pragma unroll
             for (int p = 0; p < 5; ++p) {
-                const uint32_t m = 0x00030003u << (2 * p);
-                ac[p] = mfma(a[2 * p], lo & m, ac[p]);
-                ac[p] = mfma(a[2 * p + 1], hi & m, ac[p]);
+                ac[0] = mfma(a[2 * p], u32x4{dg[0][p], dg[1][p], dg[2][p], dg[3][p]}, ac[0]);
+                ac[1] = mfma(a[2 * p + 1], u32x4{dg[4][p], dg[5][p], dg[6][p], dg[7][p]}, ac[1]);
             }
         }
     };
@@ -246,10 +237,10 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
     // (5) merge classes (every row of a D tile is the same; row 0 is element 0 of lanes 0..15),
     //     add the waves' partial sums in a fixed order, subtract sum_k x, scale, round
     auto merge = [&](const float4_t (&ac)[NCLS]) __attribute__((always_inline)) {
+        if constexpr (!TWO) return ac[0] + ac[1];
         float4_t t = ac[0] + 0.25f * ac[1];
         t += 0.0625f * ac[2] + 0.015625f * ac[3];
-        t += 0.00390625f * ac[4];
-        if constexpr (TWO) t += 0.0009765625f * ac[5];
+        t += 0.00390625f * ac[4] + 0.0009765625f * ac[5];
         return t;
     };
     float xw[1] = {xsum};

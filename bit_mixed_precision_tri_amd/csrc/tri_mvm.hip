@@ -5,8 +5,9 @@
 //   Y[m][n] = scale * sum_k t[n][k] * X[m][k],  t in {-1, 0, +1},  fp32 accumulation.
 // v_mfma_f32_16x16x32_f16 takes the (up to) 16 activation rows as its A operand and 16 weight
 // rows, decoded in registers, as B.  The decode is the one of the M = 1 kernel (tri_mv1.hip):
-// masked digits d = t + 1 read as exact fp16 values d * 4^p * 2^-24, one MFMA and one
-// accumulator per position class, classes merged with exact powers of two, and
+// digits d = t + 1 read as exact fp16 values (2-bit: masked in place, d * 4^p * 2^-24, one
+// accumulator per position class, merged with exact powers of two; 1.6-bit: base-3 digits
+// from multiply-shift quotients, d * 2^-24, one accumulator per half chunk), and
 // sum_k X[m][k] subtracted once per output at the end.
 //
 // Work split.  A workgroup of NW waves owns 16 weight rows; wave w takes chunk-steps s, where
@@ -67,13 +68,12 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
     constexpr bool TWO = FMT == TRI_FMT_2BIT;
     constexpr int XH = TWO ? 64 : 80;            // activations per chunk
     constexpr int NOP = TWO ? 8 : 10;            // A operands (MFMAs) per chunk
-    constexpr int NCLS = TWO ? 6 : 5;            // position classes
+    constexpr int NCLS = TWO ? 6 : 2;            // accumulators: position classes (2-bit), halves (1.6-bit)
     constexpr int RP = 4 * XH / 8;               // 16-byte pieces of one row per step (32 or 40)
     constexpr int NLD = (MT * RP + 63) / 64;     // whole-line activation loads per lane and step
     constexpr int RPP = RP + 1;                  // padded row stride: the 16 rows a read touches fall in distinct banks
     constexpr int XROWS = MT + (NORM ? 1 : 0);   // (+ the norm gain of the step's chunks)
     __shared__ u32x4 xraw[NW][XROWS * RPP];      // per wave: one step's activations, row-major
-    __shared__ uint32_t lut[TWO ? 1 : 256];
     __shared__ float red[NW][16][NORM ? 18 : 17];    // per wave: partial tile [row m][column j], + sum x (+ sum x^2)
     __shared__ float red1[PAIR ? NW : 1][16][17];    // pair: the second matrix's partial tile
 
@@ -83,11 +83,6 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
     const int j = lane & 15;
     const int n0 = ((int)blockIdx.x - gr.blk[gi]) * 16;
     const int64_t S = (int64_t)C * 16;
-
-    if constexpr (!TWO) {
-        for (int b = threadIdx.x; b < 256; b += 64 * NW) lut[b] = base3_digits_2bit((uint32_t)b);
-        __syncthreads();
-    }
 
     // every weight chunk of the wave, all in flight at once
     const int rows_here = min(16, N - n0);
@@ -143,19 +138,15 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
             ac[0] = mfma(a[6], u & 0x00030003u, ac[0]);
             ac[1] = mfma(a[7], u & 0x000C000Cu, ac[1]);
         } else {
-            u32x4 lo, hi;
+            // register q: bytes q and q+8, position p pairs trits (5q+p, 5q+40+p); every digit
+            // carries the same scale, so the halves accumulate in ac[0] and ac[1]
+            uint32_t dg[8][5];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const uint32_t blo = (v[q >> 2] >> (8 * (q & 3))) & 0xFFu;
-                const uint32_t bhi = (v[2 + (q >> 2)] >> (8 * (q & 3))) & 0xFFu;
-                const uint32_t pq = lut[blo] | (lut[bhi] << 16);
-                if (q < 4) lo[q] = pq; else hi[q - 4] = pq;
-            }
+            for (int q = 0; q < 8; ++q) base3_digits_u16x2(byte_pair(v, q), dg[q]);
 #pragma unroll
             for (int p = 0; p < 5; ++p) {
-                const uint32_t m = 0x00030003u << (2 * p);
-                ac[p] = mfma(a[2 * p], lo & m, ac[p]);
-                ac[p] = mfma(a[2 * p + 1], hi & m, ac[p]);
+                ac[0] = mfma(a[2 * p], u32x4{dg[0][p], dg[1][p], dg[2][p], dg[3][p]}, ac[0]);
+                ac[1] = mfma(a[2 * p + 1], u32x4{dg[4][p], dg[5][p], dg[6][p], dg[7][p]}, ac[1]);
             }
         }
     };
@@ -229,10 +220,10 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
 
     // merge classes: lane (g, j) holds rows 4g + e of column j (of D and of the sums of X)
     auto merge = [&](const float4_t (&ac)[NCLS]) __attribute__((always_inline)) {
+        if constexpr (!TWO) return ac[0] + ac[1];
         float4_t t = ac[0] + 0.25f * ac[1];
         t += 0.0625f * ac[2] + 0.015625f * ac[3];
-        t += 0.00390625f * ac[4];
-        if constexpr (TWO) t += 0.0009765625f * ac[5];
+        t += 0.00390625f * ac[4] + 0.0009765625f * ac[5];
         return t;
     };
     const float4_t t = merge(acc);
