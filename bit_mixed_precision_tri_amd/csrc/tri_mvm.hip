@@ -84,21 +84,6 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
     const int n0 = ((int)blockIdx.x - gr.blk[gi]) * 16;
     const int64_t S = (int64_t)C * 16;
 
-    // every weight chunk of the wave, all in flight at once
-    const int rows_here = min(16, N - n0);
-    const __amdgpu_buffer_rsrc_t wr =
-        rsrc(Wp + (int64_t)n0 * S, __builtin_amdgcn_readfirstlane((uint32_t)(rows_here * S)));
-    // (pair: the same chunks of the second matrix, requested in the order they are used)
-    const __amdgpu_buffer_rsrc_t wr1 =
-        rsrc(gr.Wp[PAIR ? 1 : 0] + (int64_t)n0 * S, __builtin_amdgcn_readfirstlane((uint32_t)(rows_here * S)));
-    u32x4 wq[CST], wq1[PAIR ? CST : 1];
-#pragma unroll
-    for (int s = 0; s < CST; ++s) {
-        const int c = 4 * (s * NW + wv) + g;
-        const int off = c < C ? (int)(uint32_t)(j * S + c * 16) : (int)0x80000000u;
-        wq[s] = __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 0);
-        if constexpr (PAIR) wq1[s] = __builtin_amdgcn_raw_buffer_load_b128(wr1, off, 0, 0);
-    }
     // activations of step s: piece P = 64i + lane is piece P % RP of row P / RP, i.e. values
     // 16*(4*(s*NW + w)*XH/16 + P % RP) ... of that row: whole 128-byte lines per instruction
     const __amdgpu_buffer_rsrc_t xr = rsrc(X, __builtin_amdgcn_readfirstlane((uint32_t)((int64_t)M * K * 2)));
@@ -152,12 +137,29 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
     };
     float4_t accx = zero4;                       // sum_k X[m][k] in every column of the tile
     float xsq = 0.f;                             // norm: sum of x^2 over this lane's values of row j
-    // the activations of PD steps are in flight at once (a ring of register sets; one step
-    // ahead measured best: deeper rings gained nothing)
-    constexpr int PD = 1;
+    // the activations of PD steps are in flight at once (a ring of register sets).  The first
+    // PD steps' activations are requested before the weights: the load counter is in order,
+    // so the first steps' bounce and permutation overlap the weight stream instead of waiting
+    // behind it (two steps measured best; deeper rings gained about 1%)
+    constexpr int PD = 2;
     u32x4 xv[PD][NLD], nv[PD];
 #pragma unroll
     for (int t = 0; t < PD; ++t) load_x(t, xv[t], nv[t]);
+    // every weight chunk of the wave, all in flight at once
+    const int rows_here = min(16, N - n0);
+    const __amdgpu_buffer_rsrc_t wr =
+        rsrc(Wp + (int64_t)n0 * S, __builtin_amdgcn_readfirstlane((uint32_t)(rows_here * S)));
+    // (pair: the same chunks of the second matrix, requested in the order they are used)
+    const __amdgpu_buffer_rsrc_t wr1 =
+        rsrc(gr.Wp[PAIR ? 1 : 0] + (int64_t)n0 * S, __builtin_amdgcn_readfirstlane((uint32_t)(rows_here * S)));
+    u32x4 wq[CST], wq1[PAIR ? CST : 1];
+#pragma unroll
+    for (int s = 0; s < CST; ++s) {
+        const int c = 4 * (s * NW + wv) + g;
+        const int off = c < C ? (int)(uint32_t)(j * S + c * 16) : (int)0x80000000u;
+        wq[s] = __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 0);
+        if constexpr (PAIR) wq1[s] = __builtin_amdgcn_raw_buffer_load_b128(wr1, off, 0, 0);
+    }
 #pragma unroll
     for (int s = 0; s < CST; ++s) {
         if (4 * (s * NW + wv) >= C) break;       // wave-uniform: no chunk of this step is live
