@@ -76,7 +76,6 @@ __device__ __forceinline__ uint32_t digits_to_t(uint32_t w, uint32_t bias)
 constexpr int kBM = 128;             // rows of Y per workgroup
 constexpr int kMT = 4;               // 32-row MFMA tiles per wave
 constexpr int kBN = 512;             // columns of Y per tile (4 waves side by side, 4 MFMA tiles each)
-constexpr int kCUs = 256;            // workgroups the chip runs at once (one per CU)
 
 // A workgroup computes one 128 x 512 tile of Y (NT = 4) or one half of it, 128 x 256 (NT = 2),
 // tile_base + blockIdx.x (NT = 4) or tile_base + blockIdx.x / 2 (NT = 2) in the tile order.

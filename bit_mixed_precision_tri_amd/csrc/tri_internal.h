@@ -6,6 +6,8 @@
 
 namespace tri {
 
+constexpr int kCUs = 256;                        // compute units of an MI355X
+
 inline int64_t row_bytes(int64_t K, int fmt)
 {
     if (K < 1) return -1;

@@ -86,7 +86,8 @@ def test_small_layer_both_formats_all_algos():
 RAGGED = [(1, 1, 1), (1, 37, 1000), (1, 130, 4097), (1, 300, 81), (1, 33, 12000), (2, 17, 65), (3, 129, 333),
           (5, 300, 81), (16, 50, 4097), (16, 1, 160), (7, 1025, 640), (17, 40, 200), (40, 70, 700),
           (64, 96, 513), (130, 257, 1111), (129, 300, 1000), (200, 513, 2048), (256, 260, 328),
-          (150, 100, 64), (96, 600, 320), (33, 700, 1088)]
+          (150, 100, 64), (96, 600, 320), (33, 700, 1088),
+          (13, 4200, 1000), (16, 4111, 2000), (12, 4500, 4096)]   # > 256 row blocks of 16 rows
 
 
 @pytest.mark.parametrize("fmt", FMTS)
