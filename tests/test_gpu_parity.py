@@ -101,6 +101,24 @@ def test_layer_ragged_shapes(fmt, shape):
         check_layer(run_layer(X, Wp, s, K, fmt, algo), X, W, s, "M=%d N=%d K=%d fmt=%d algo=%d" % (M, N, K, fmt, algo))
 
 
+def test_every_1p6bit_byte_value_in_the_layer():
+    """Rows made of all 243 five-trit patterns (each byte value of the 1.6-bit packing once per
+    row, in a row-dependent order): every kernel family decodes every byte value."""
+    import itertools
+    pats = np.array(list(itertools.product((-1, 0, 1), repeat=5)), dtype=np.int8)   # (243, 5)
+    N, K = 40, 1280                              # K % 8 == 0: the MFMA decode kernels serve M <= 16
+    W = synth.trits(synth.rng_for(231, 0, 0), N, K)
+    W[:, :243 * 5] = np.stack([np.roll(pats, 7 * n, axis=0).reshape(-1) for n in range(N)])
+    Wp = tri.pack(cuda(W), tri.TRI_FMT_1P6BIT)
+    rows = oracle.pack(W, tri.TRI_FMT_1P6BIT)
+    assert sorted(set(rows[0][:243].tolist())) == list(range(243))
+    for M in (1, 4, 16, 33):
+        X = synth.activations(synth.rng_for(230, M, 0), M, K)
+        for algo in algos_for(M, tri.TRI_FMT_1P6BIT):
+            Y = run_layer(X, Wp, 0.02, K, tri.TRI_FMT_1P6BIT, algo)
+            check_layer(Y, X, W, 0.02, "all bytes M=%d algo=%d" % (M, algo))
+
+
 def test_special_values():
     """Zero weights, all +1 weights, a one-hot activation, a negative scale, fp16 extremes.
     (The scales keep every |Y| below the fp16 range; overflow is covered by test_overflow_to_inf.)"""
