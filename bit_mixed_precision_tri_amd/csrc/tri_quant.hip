@@ -16,10 +16,11 @@
 //                    writes one partial sum to the workspace (fixed order, no atomics);
 //   k_absmean_final  one workgroup adds the partial sums in a fixed order and writes the
 //                    float32 scale to device memory;
-//   k_quant_pack     one thread per packed byte: reads the scale, decides its 4 (2-bit) or
-//                    5 (1.6-bit) trits and writes the byte in the layout of tri_pack2 /
-//                    tri_pack16 (digit t+1, lowest k least significant, rows padded with
-//                    zero trits to whole 16-byte chunks).
+//   k_quant_pack*    reads the scale, decides the trits and writes the packed bytes in the
+//                    layout of tri_pack2 / tri_pack16 (digit t+1, lowest k least significant,
+//                    rows padded with zero trits to whole 16-byte chunks): with 16-byte weight
+//                    loads when K % 4 == 0 (one byte per thread for 2-bit, four for 1.6-bit),
+//                    else one thread per byte with single loads.
 // The result is deterministic: the same input gives the same scale and bytes on every run.
 #include "tri_device.h"
 #include "tri_internal.h"
@@ -118,6 +119,71 @@ __global__ __launch_bounds__(kThreads) void k_quant_pack(const float *__restrict
     }
 }
 
+// The same with whole 16-byte weight loads, for K % 4 == 0 (every row starts 16-byte aligned):
+// 2-bit, one thread per packed byte and one load per byte; 1.6-bit, one thread per four packed
+// bytes (20 weights, five loads) written as one 32-bit word (a row's bytes are a multiple of 16,
+// so a group never straddles two rows).
+__device__ __forceinline__ uint32_t digit_of_weight(float w, float g)
+{
+    return (g > 0.f && 2.f * fabsf(w) > g) ? (w > 0.f ? 2u : 0u) : 1u;
+}
+
+__global__ __launch_bounds__(kThreads) void k_quant_pack2_v(const float *__restrict__ W, int64_t N, int64_t K,
+                                                            int64_t S, const float *__restrict__ scale,
+                                                            uint8_t *__restrict__ Wp)
+{
+    const float g = scale[0];
+    const int64_t total = N * S;
+    for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t n = idx / S;
+        const int64_t b = idx - n * S;
+        uint32_t value = 1u | (1u << 2) | (1u << 4) | (1u << 6);   // four zero trits (row padding)
+        if (4 * b < K) {
+            const float4 v = *reinterpret_cast<const float4 *>(W + n * K + 4 * b);
+            value = digit_of_weight(v.x, g) | (digit_of_weight(v.y, g) << 2) | (digit_of_weight(v.z, g) << 4) |
+                    (digit_of_weight(v.w, g) << 6);
+        }
+        Wp[idx] = (uint8_t)value;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_quant_pack16_v(const float *__restrict__ W, int64_t N, int64_t K,
+                                                             int64_t S, const float *__restrict__ scale,
+                                                             uint8_t *__restrict__ Wp)
+{
+    const float g = scale[0];
+    const int64_t S4 = S / 4;
+    const int64_t total = N * S4;
+    for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t n = idx / S4;
+        const int64_t b0 = 4 * (idx - n * S4);      // first of the four bytes
+        const int64_t k0 = 5 * b0;                  // its first trit
+        float w[20];
+        if (k0 + 20 <= K) {
+            const float4 *q = reinterpret_cast<const float4 *>(W + n * K + k0);
+#pragma unroll
+            for (int i = 0; i < 5; ++i) {
+                const float4 v = q[i];
+                w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 20; ++i) w[i] = (k0 + i < K) ? W[n * K + k0 + i] : 0.f;   // past K: zero trits
+        }
+        uint32_t word = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            uint32_t value = 0;
+#pragma unroll
+            for (int j = 4; j >= 0; --j) value = value * 3u + digit_of_weight(w[5 * q + j], g);
+            word |= value << (8 * q);
+        }
+        *reinterpret_cast<uint32_t *>(Wp + n * S + b0) = word;
+    }
+}
+
 int launch_quantize(const float *W, int64_t N, int64_t K, int fmt, uint8_t *Wp, float *scale, void *workspace,
                     hipStream_t s)
 {
@@ -128,6 +194,16 @@ int launch_quantize(const float *W, int64_t N, int64_t K, int fmt, uint8_t *Wp, 
     hipLaunchKernelGGL(k_absmean_part, dim3(P), dim3(kThreads), 0, s, W, E, per, part);
     hipLaunchKernelGGL(k_absmean_final, dim3(1), dim3(kThreads), 0, s, part, P, E, scale);
     const int64_t S = row_bytes(K, fmt);
+    if (K % 4 == 0) {                                    // 16-byte aligned rows: vector loads
+        const int64_t items = fmt == TRI_FMT_2BIT ? N * S : N * S / 4;
+        int64_t vb = (items + kThreads - 1) / kThreads;
+        if (vb > 65536) vb = 65536;                      // grid-stride loop covers the rest
+        if (fmt == TRI_FMT_2BIT)
+            hipLaunchKernelGGL(k_quant_pack2_v, dim3((unsigned)vb), dim3(kThreads), 0, s, W, N, K, S, scale, Wp);
+        else
+            hipLaunchKernelGGL(k_quant_pack16_v, dim3((unsigned)vb), dim3(kThreads), 0, s, W, N, K, S, scale, Wp);
+        return hipGetLastError() == hipSuccess ? TRI_OK : TRI_EHIP;
+    }
     int64_t blocks = (N * S + kThreads - 1) / kThreads;
     if (blocks > 65536) blocks = 65536;                  // grid-stride loop covers the rest
     if (fmt == TRI_FMT_2BIT)
