@@ -465,10 +465,27 @@ def bench_prefill(clock):
     for fmt in cfg["fmts"]:
         for li, (name, K, N) in enumerate(cfg["shapes"]):
             L = Layer(cfg["workload_id"], li, cfg["M"], N, K, fmt, cfg["scale"], copies=1)
-            t, _ = clock.run([L.launch] * 12, warmup=2)
+            # the GEMM is compute-bound: after idle time the GPU runs it at a lower clock for tens of
+            # milliseconds, so it runs back to back for half a second before it is timed (the
+            # sustained rate of a long prefill)
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < 0.5:
+                for _ in range(8):
+                    L.launch()
+                torch.cuda.synchronize()
+            # (timed with plain events: a launch takes ~1 ms, far longer than the host needs to queue
+            # it, and an idle sleep kernel in front would let the clock drop again)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(20):
+                L.launch()
+            b.record()
+            torch.cuda.synchronize()
+            t = a.elapsed_time(b) / 1e3 / 20
             tf = L.flops / t / 1e12
             res.append({"shape": name, "M": cfg["M"], "format": configs.FMT_NAMES[fmt], "kernel_us": round(t * 1e6, 2),
-                        "TFLOPs": round(tf, 2), "frac_mfma": round(tf / MFMA_F16_PEAK_TFLOPS, 4)})
+                        "TFLOPs": round(tf, 2), "frac_mfma": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+                        "timing": "events around 20 back-to-back launches, after 0.5 s of the same GEMM"})
             del L
             torch.cuda.empty_cache()
     return res
