@@ -282,10 +282,13 @@ def main():
                    "M": 1, "shapes": [[K, N] for (_, K, N) in dcfg["shapes"]], "format": "2bit",
                    "accumulate": "f32", "bytes_per_step": step_bytes, "timing": "HIP graph replay"},
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        # per launch, averaged over the three decode shapes (one launch each per step)
         "roofline": {"bound": "hbm", "kernel": "k_mv1 (tri_mv1.hip)", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": (ctr or {}).get("traffic_bytes_per_step"),
-                     "algorithmic_bytes": step_bytes, "launches": len(per_launch),
+                     "traffic": (round(ctr["traffic_bytes_per_step"] / len(per_launch)) if ctr else None),
+                     "algorithmic_bytes": round(step_bytes / len(per_launch)),
+                     "per": "launch, mean over the three decode shapes",
+                     "launches_per_step": len(per_launch),
                      "mean_launch_us": round(sum(per_launch) / len(per_launch) * 1e6, 3), "queue_ahead": ahead},
         "context": "the pages report relative speed-ups only, on NVIDIA GPUs: TriRun up to 5x end-to-end generation "
                    "vs PyTorch FP16 on an L40S (64+64 tokens), about 8x per ternary layer; no absolute GB/s or "
