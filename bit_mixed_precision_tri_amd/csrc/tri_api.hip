@@ -26,10 +26,28 @@ int check_linear(const void *X, const void *Wp, int64_t M, int64_t N, int64_t K,
     return TRI_OK;
 }
 
-int select_algo(int64_t M, int fmt)
+// The kernel family for a shape.  Up to 16 rows, the small-M kernels (at M = 1 the MFMA kernel
+// beats the VALU GEMV).  Above, the small-M kernels take one pass over the weights per 16-row
+// slice of X, while the GEMM's parallelism comes from its 128 x 512 output tiles alone, so with
+// few tiles most CUs idle.  Both costs per unit of K, from fits to measured times on MI355X
+// (M = 17 .. 512; K x N = 4096 x 4096, 4096 x 11008, 11008 x 4096, 8192 x 28672, 28672 x 8192;
+// both formats):
+//   small-M  ceil(M/16) * N * c,  c = 0.10 ps (2-bit) / 0.15 ps (1.6-bit) per trit and slice;
+//            rows too long for the eight-wave kernels run 4.5x / 1.9x slower;
+//   GEMM     u * R,  u = 11 ns (2-bit) / 13.3 ns (1.6-bit) per round of half-width tiles,
+//            R = the rounds of its launch (a last round of at most 128 tiles runs at half width).
+int select_algo(int64_t M, int64_t N, int64_t K, int fmt)
 {
-    if (M <= 16) return TRI_ALGO_SMALLM;          // (at M = 1 the MFMA kernel beats the VALU GEMV)
-    return TRI_ALGO_GEMM;
+    if (M <= 16) return TRI_ALGO_SMALLM;
+    const bool two = fmt == TRI_FMT_2BIT;
+    double c = two ? 0.10 : 0.15;                // ps
+    if (K > (two ? 16384 : 20480)) c *= two ? 4.5 : 1.9;
+    const int64_t T = ((M + 127) / 128) * ((N + 511) / 512);
+    const int64_t r = T % kCUs;
+    const int64_t R = (r > 0 && r <= kCUs / 2) ? 2 * (T / kCUs) + 1 : 2 * ((T + kCUs - 1) / kCUs);
+    const double small = (double)((M + 15) / 16) * (double)N * c;
+    const double gemm = (two ? 11000.0 : 13300.0) * (double)R;
+    return small < gemm ? TRI_ALGO_SMALLM : TRI_ALGO_GEMM;
 }
 
 int run_linear(const _Float16 *X, const uint8_t *Wp, float scale, int64_t M, int64_t N, int64_t K, int fmt,
@@ -42,7 +60,19 @@ int run_linear(const _Float16 *X, const uint8_t *Wp, float scale, int64_t M, int
         if (M != 1 || fmt != TRI_FMT_2BIT) return TRI_EINVAL;
         return launch_gemv2(x, Wp, scale, (int)N, (int)K, y, s);
     case TRI_ALGO_SMALLM:
-        if (M > 16) return TRI_EINVAL;
+        if (M > 16) {
+            // one launch over 16-row slices of X where the batched kernel serves the shape,
+            // else one small-M call per slice
+            int n = (int)N;
+            const Groups gr = make_groups(1, &Wp, &scale, &n, &y);
+            if (launch_mvm(x, gr, (int)M, (int)K, fmt, s)) return hipGetLastError() == hipSuccess ? TRI_OK : TRI_EHIP;
+            for (int64_t m0 = 0; m0 < M; m0 += 16) {
+                const int64_t mm = (M - m0) < 16 ? (M - m0) : 16;
+                const int rc = run_linear(X + m0 * K, Wp, scale, mm, N, K, fmt, Y + m0 * N, TRI_ALGO_SMALLM, s);
+                if (rc != TRI_OK) return rc;
+            }
+            return TRI_OK;
+        }
         if (launch_decode(x, Wp, scale, (int)M, (int)N, (int)K, fmt, y, s))
             return hipGetLastError() == hipSuccess ? TRI_OK : TRI_EHIP;
         return launch_smallm(x, Wp, scale, (int)M, (int)N, (int)K, fmt, y, s);   // long rows: streaming variant
@@ -98,14 +128,14 @@ int tri_unpack(const uint8_t *Wp, int64_t N, int64_t K, int fmt, int8_t *W, hipS
 int tri_select_algo(int64_t M, int64_t N, int64_t K, int fmt)
 {
     if (M < 1 || N < 1 || K < 1 || !known_fmt(fmt) || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return TRI_EINVAL;
-    return select_algo(M, fmt);
+    return select_algo(M, N, K, fmt);
 }
 
 int tri_linear(const _Float16 *X, const uint8_t *Wp, float scale, int64_t M, int64_t N, int64_t K, int fmt,
                _Float16 *Y, hipStream_t stream)
 {
     const int rc = check_linear(X, Wp, M, N, K, fmt, Y);
-    return rc != TRI_OK ? rc : run_linear(X, Wp, scale, M, N, K, fmt, Y, select_algo(M, fmt), stream);
+    return rc != TRI_OK ? rc : run_linear(X, Wp, scale, M, N, K, fmt, Y, select_algo(M, N, K, fmt), stream);
 }
 
 int tri_linear_algo(const _Float16 *X, const uint8_t *Wp, float scale, int64_t M, int64_t N, int64_t K, int fmt,
@@ -113,7 +143,7 @@ int tri_linear_algo(const _Float16 *X, const uint8_t *Wp, float scale, int64_t M
 {
     const int rc = check_linear(X, Wp, M, N, K, fmt, Y);
     if (rc != TRI_OK) return rc;
-    if (algo == TRI_ALGO_AUTO) algo = select_algo(M, fmt);
+    if (algo == TRI_ALGO_AUTO) algo = select_algo(M, N, K, fmt);
     return run_linear(X, Wp, scale, M, N, K, fmt, Y, algo, stream);
 }
 
@@ -129,7 +159,9 @@ int tri_linear_grouped(const _Float16 *X, const uint8_t *const *Wp, const float 
     for (int g = 0; g < G; ++g) blocks += (N[g] + 15) / 16;
     if (blocks >= ((int64_t)1 << 31)) return TRI_EINVAL;
     const uint16_t *x = reinterpret_cast<const uint16_t *>(X);
-    if (M <= 16) {
+    bool small = true;                           // every matrix on the small-M kernels
+    for (int g = 0; g < G; ++g) small = small && select_algo(M, N[g], K, fmt) == TRI_ALGO_SMALLM;
+    if (small) {
         int n[kMaxGroups];
         uint16_t *y[kMaxGroups];
         for (int g = 0; g < G; ++g) {
@@ -140,9 +172,9 @@ int tri_linear_grouped(const _Float16 *X, const uint8_t *const *Wp, const float 
         const bool done = M == 1 ? launch_mv1(x, gr, (int)K, fmt, stream) : launch_mvm(x, gr, (int)M, (int)K, fmt, stream);
         if (done) return hipGetLastError() == hipSuccess ? TRI_OK : TRI_EHIP;
     }
-    // shapes outside the grouped kernels' range (and M > 16): one launch per matrix
+    // shapes outside the grouped kernels' range: one call per matrix
     for (int g = 0; g < G; ++g) {
-        const int rc = run_linear(X, Wp[g], scale[g], M, N[g], K, fmt, Y[g], select_algo(M, fmt), stream);
+        const int rc = run_linear(X, Wp[g], scale[g], M, N[g], K, fmt, Y[g], select_algo(M, N[g], K, fmt), stream);
         if (rc != TRI_OK) return rc;
     }
     return TRI_OK;

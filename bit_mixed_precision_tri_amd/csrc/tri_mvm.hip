@@ -1,5 +1,6 @@
 // tri_mvm.hip -- ternary linear layer for a few activation rows (2 <= M <= 16, batched decode)
-// on MFMA.
+// on MFMA; more rows run as 16-row slices in one launch (a second grid dimension), the weights
+// of a row block then being read once per slice.
 //
 // The layer (Pith review of "Spectra 1.1", "What carries the argument"):
 //   Y[m][n] = scale * sum_k t[n][k] * X[m][k],  t in {-1, 0, +1},  fp32 accumulation.
@@ -54,17 +55,23 @@ __device__ __forceinline__ void wave_sync()
 
 }  // namespace
 
-template <int FMT, int MT, int NW, int CST, int GL>
+template <int FMT, int MT, int NW, int CST, int GL, int RB>
 __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X, const Groups gr, int M, int K, int C,
                                                  const Fusion fu)
 {
     constexpr bool NORM = (GL & kGlueNorm) != 0;
     constexpr bool PAIR = (GL & kGluePair) != 0;
+    static_assert(GL == 0 || RB == 1, "the glue variants own one 16-row block per workgroup");
     const int gi = group_of(gr, (int)blockIdx.x);
     const uint8_t *__restrict__ Wp = gr.Wp[gi];
-    uint16_t *__restrict__ Y = gr.Y[gi];
     const float scale = gr.scale[gi];
     const int N = gr.N[gi];
+    // more than 16 activation rows: workgroup row y of the grid takes rows 16y .. 16y+15 of X and Y
+    const int64_t m_first = 16 * (int64_t)blockIdx.y;
+    X += m_first * K;
+    M = min(16, M - (int)m_first);
+    uint16_t *__restrict__ Y = gr.Y[gi] + m_first * N;
+    const uint16_t *__restrict__ R = fu.res[gi] ? fu.res[gi] + m_first * N : nullptr;
     constexpr bool TWO = FMT == TRI_FMT_2BIT;
     constexpr int XH = TWO ? 64 : 80;            // activations per chunk
     constexpr int NOP = TWO ? 8 : 10;            // A operands (MFMAs) per chunk
@@ -73,15 +80,20 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
     constexpr int NLD = (MT * RP + 63) / 64;     // whole-line activation loads per lane and step
     constexpr int RPP = RP + 1;                  // padded row stride: the 16 rows a read touches fall in distinct banks
     constexpr int XROWS = MT + (NORM ? 1 : 0);   // (+ the norm gain of the step's chunks)
-    __shared__ u32x4 xraw[NW][XROWS * RPP];      // per wave: one step's activations, row-major
-    __shared__ float red[NW][16][NORM ? 18 : 17];    // per wave: partial tile [row m][column j], + sum x (+ sum x^2)
+    // per wave: one step's activations, row-major; after the last step the same LDS holds the
+    // per-wave partial tiles [row m][column (block r, row j)], + sum x (+ sum x^2)
+    constexpr int RCOL = 16 * RB + (NORM ? 2 : 1);
+    constexpr int XRAW_B = NW * XROWS * RPP * 16, RED_B = NW * 16 * RCOL * 4;
+    __shared__ u32x4 smem[(XRAW_B > RED_B ? XRAW_B : RED_B) / 16];
+    u32x4 (*xraw)[XROWS * RPP] = reinterpret_cast<u32x4 (*)[XROWS * RPP]>(smem);
+    float (*red)[16][RCOL] = reinterpret_cast<float (*)[16][RCOL]>(smem);
     __shared__ float red1[PAIR ? NW : 1][16][17];    // pair: the second matrix's partial tile
 
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar descriptors)
     const int g = lane >> 4;
     const int j = lane & 15;
-    const int n0 = ((int)blockIdx.x - gr.blk[gi]) * 16;
+    const int n0 = ((int)blockIdx.x - gr.blk[gi]) * 16 * RB;
     const int64_t S = (int64_t)C * 16;
 
     // activations of step s: piece P = 64i + lane is piece P % RP of row P / RP, i.e. values
@@ -109,9 +121,11 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
     };
 
     const float4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-    float4_t acc[NCLS];
+    float4_t acc[RB][NCLS];
 #pragma unroll
-    for (int c = 0; c < NCLS; ++c) acc[c] = zero4;
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int c = 0; c < NCLS; ++c) acc[r][c] = zero4;
     float4_t acc1[PAIR ? NCLS : 1];              // pair: the second matrix
 #pragma unroll
     for (int c = 0; c < (PAIR ? NCLS : 1); ++c) acc1[c] = zero4;
@@ -146,19 +160,25 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
 #pragma unroll
     for (int t = 0; t < PD; ++t) load_x(t, xv[t], nv[t]);
     // every weight chunk of the wave, all in flight at once
-    const int rows_here = min(16, N - n0);
+    const int rows_here = min(16 * RB, N - n0);
     const __amdgpu_buffer_rsrc_t wr =
         rsrc(Wp + (int64_t)n0 * S, __builtin_amdgcn_readfirstlane((uint32_t)(rows_here * S)));
     // (pair: the same chunks of the second matrix, requested in the order they are used)
     const __amdgpu_buffer_rsrc_t wr1 =
         rsrc(gr.Wp[PAIR ? 1 : 0] + (int64_t)n0 * S, __builtin_amdgcn_readfirstlane((uint32_t)(rows_here * S)));
-    u32x4 wq[CST], wq1[PAIR ? CST : 1];
+    u32x4 wq[RB][CST], wq1[PAIR ? CST : 1];
 #pragma unroll
     for (int s = 0; s < CST; ++s) {
         const int c = 4 * (s * NW + wv) + g;
-        const int off = c < C ? (int)(uint32_t)(j * S + c * 16) : (int)0x80000000u;
-        wq[s] = __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 0);
-        if constexpr (PAIR) wq1[s] = __builtin_amdgcn_raw_buffer_load_b128(wr1, off, 0, 0);
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {           // (rows past the matrix's end read as zero)
+            const int off = c < C ? (int)(uint32_t)((16 * r + j) * S + c * 16) : (int)0x80000000u;
+            wq[r][s] = __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 0);
+        }
+        if constexpr (PAIR) {
+            const int off = c < C ? (int)(uint32_t)(j * S + c * 16) : (int)0x80000000u;
+            wq1[s] = __builtin_amdgcn_raw_buffer_load_b128(wr1, off, 0, 0);
+        }
     }
 #pragma unroll
     for (int s = 0; s < CST; ++s) {
@@ -216,7 +236,8 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
 #pragma unroll
         for (int p = 0; p < NOP; ++p) accx = mfma(a[p], ones, accx);
         // decode and contract
-        contract(a, wq[s], acc);
+#pragma unroll
+        for (int r = 0; r < RB; ++r) contract(a, wq[r][s], acc[r]);
         if constexpr (PAIR) contract(a, wq1[s], acc1);
     }
 
@@ -228,12 +249,16 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
         t += 0.00390625f * ac[4] + 0.0009765625f * ac[5];
         return t;
     };
-    const float4_t t = merge(acc);
+    __syncthreads();                             // every wave is done with its activation slot
 #pragma unroll
-    for (int e = 0; e < 4; ++e) red[wv][4 * g + e][j] = t[e];
+    for (int r = 0; r < RB; ++r) {
+        const float4_t t = merge(acc[r]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red[wv][4 * g + e][16 * r + j] = t[e];
+    }
     if (j == 0) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) red[wv][4 * g + e][16] = accx[e];
+        for (int e = 0; e < 4; ++e) red[wv][4 * g + e][16 * RB] = accx[e];
     }
     if constexpr (PAIR) {
         const float4_t t1 = merge(acc1);
@@ -242,24 +267,24 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
     }
     if constexpr (NORM) {
         const float q = sum_over_rows(xsq);      // lanes j, j+16, j+32, j+48 hold parts of row j
-        if (g == 0) red[wv][j][17] = q;
+        if (g == 0) red[wv][j][16 * RB + 1] = q;
     }
     __syncthreads();
     // thread (m, jj): output Y[m][n0 + jj], waves added in a fixed order
-    for (int o = threadIdx.x; o < MT * 16; o += 64 * NW) {
-        const int m = o >> 4, jj = o & 15;
+    for (int o = threadIdx.x; o < MT * 16 * RB; o += 64 * NW) {
+        const int m = o / (16 * RB), jj = o % (16 * RB);
         if (m < M && n0 + jj < N) {
             float sd = 0.f, sx = 0.f;
 #pragma unroll
             for (int w = 0; w < NW; ++w) {
                 sd += red[w][m][jj];
-                sx += red[w][m][16];
+                sx += red[w][m][16 * RB];
             }
             float rinv = 1.f;
             if constexpr (NORM) {
                 float sq = 0.f;
 #pragma unroll
-                for (int w = 0; w < NW; ++w) sq += red[w][m][17];
+                for (int w = 0; w < NW; ++w) sq += red[w][m][16 * RB + 1];
                 rinv = 1.f / sqrtf(sq / (float)K + fu.eps);
             }
             float y = (sd * 16777216.0f - sx) * scale * rinv;
@@ -270,7 +295,7 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
                 const float y1 = (sd1 * 16777216.0f - sx) * gr.scale[1] * rinv;
                 y = y / (1.f + __expf(-y)) * y1; // silu(gate) * up
             }
-            if (fu.res[gi]) y += h2f(fu.res[gi][(int64_t)m * N + n0 + jj]);
+            if (R) y += h2f(R[(int64_t)m * N + n0 + jj]);
             Y[(int64_t)m * N + n0 + jj] = __builtin_bit_cast(uint16_t, (_Float16)y);
         }
     }
@@ -289,37 +314,79 @@ constexpr bool has_glue()
     return true;
 }
 
-template <int FMT, int MT, int NW, int CST, int GL>
+// Several 16-row blocks per workgroup (RB): every activation value a wave reads feeds RB
+// blocks, so the activations are re-read from cache RB times less often.  Variants exist for
+// eight waves without glue, and only where the weight registers do not spill.
+template <int FMT, int MT, int CST, int RB>
+constexpr bool has_rb()
+{
+    if (RB == 1) return true;
+    if (RB == 2) return FMT == TRI_FMT_2BIT ? CST <= 8 : (MT == 16 ? CST <= 5 : CST <= 6);
+    if (RB == 4) return FMT == TRI_FMT_2BIT && (MT == 16 ? CST <= 3 : MT == 8 ? CST <= 4 : CST <= 5);
+    return false;
+}
+
+// The grid of RB-block workgroups: matrix g owns workgroups blk[g] .. blk[g+1]-1.
+Groups regroup(const Groups &gr, int RB)
+{
+    Groups g = gr;
+    for (int q = 0; q < gr.G; ++q) g.blk[q + 1] = g.blk[q] + (gr.N[q] + 16 * RB - 1) / (16 * RB);
+    for (int q = gr.G; q < kMaxGroups; ++q) g.blk[q + 1] = g.blk[gr.G];
+    return g;
+}
+
+// Blocks per workgroup: the largest RB whose grid (over every 16-row slice of the activations)
+// still gives 5/8 of a workgroup per CU.  Fewer, fuller workgroups win down to about that
+// point (measured at M = 4..64 on 4096 -> 11008, 11008 -> 4096 and 4096 -> 4096: 172
+// four-block workgroups beat 688 one-block ones by 15-25%; 128 lose to 256).
+int choose_rb(const Groups &gr, int M)
+{
+    const int64_t slices = (M + 15) / 16;
+    for (int rb = 4; rb > 1; rb /= 2)
+        if (regroup(gr, rb).blk[gr.G] * slices >= kCUs * 5 / 8) return rb;
+    return 1;
+}
+
+template <int FMT, int MT, int NW, int CST, int GL, int RB>
 static bool launch_gl(const uint16_t *X, const Groups &gr, int M, int K, int C, hipStream_t s, const Fusion &f)
 {
-    if constexpr (has_glue<FMT, MT, NW, CST, GL>()) {
-        hipLaunchKernelGGL((k_mvm<FMT, MT, NW, CST, GL>), dim3(gr.blk[gr.G]), dim3(64 * NW), 0, s, X, gr, M, K, C, f);
+    if constexpr (has_glue<FMT, MT, NW, CST, GL>() && has_rb<FMT, MT, CST, RB>()) {
+        const Groups g = RB == 1 ? gr : regroup(gr, RB);
+        hipLaunchKernelGGL((k_mvm<FMT, MT, NW, CST, GL, RB>), dim3(g.blk[g.G], (M + 15) / 16), dim3(64 * NW), 0, s, X,
+                           g, M, K, C, f);
         return true;
     }
     return false;
 }
 
 template <int FMT, int MT, int NW, int CST>
-static bool launch_cfg(const uint16_t *X, const Groups &gr, int M, int K, int C, hipStream_t s, const Fusion *fu)
+static bool launch_cfg(const uint16_t *X, const Groups &gr, int M, int K, int C, hipStream_t s, const Fusion *fu,
+                       int rb = 1)
 {
     const Fusion f = fu ? *fu : Fusion{};
     switch (glue_bits(fu)) {
-    case kGlueNorm: return launch_gl<FMT, MT, NW, CST, kGlueNorm>(X, gr, M, K, C, s, f);
-    case kGluePair: return launch_gl<FMT, MT, NW, CST, kGluePair>(X, gr, M, K, C, s, f);
-    case kGlueNorm | kGluePair: return launch_gl<FMT, MT, NW, CST, kGlueNorm | kGluePair>(X, gr, M, K, C, s, f);
-    default: return launch_gl<FMT, MT, NW, CST, 0>(X, gr, M, K, C, s, f);
+    case kGlueNorm: return launch_gl<FMT, MT, NW, CST, kGlueNorm, 1>(X, gr, M, K, C, s, f);
+    case kGluePair: return launch_gl<FMT, MT, NW, CST, kGluePair, 1>(X, gr, M, K, C, s, f);
+    case kGlueNorm | kGluePair: return launch_gl<FMT, MT, NW, CST, kGlueNorm | kGluePair, 1>(X, gr, M, K, C, s, f);
+    default:
+        if constexpr (NW == 8) {                 // the largest RB up to rb that has a variant
+            if (rb >= 4 && launch_gl<FMT, MT, NW, CST, 0, 4>(X, gr, M, K, C, s, f)) return true;
+            if (rb >= 2 && launch_gl<FMT, MT, NW, CST, 0, 2>(X, gr, M, K, C, s, f)) return true;
+        }
+        return launch_gl<FMT, MT, NW, CST, 0, 1>(X, gr, M, K, C, s, f);
     }
 }
 
 template <int FMT, int MT>
 static bool launch_mt(const uint16_t *X, const Groups &gr, int M, int K, int C, hipStream_t s,
-                      const Fusion *fu)
+                      const Fusion *fu, int rb)
 {
     // 1.6-bit tiles of 16 rows: an eight-wave workgroup's activation slots take about 93 KB of LDS,
-    // so one workgroup fits a CU; with more row blocks than CUs, four-wave workgroups (half the
-    // LDS) let two share a CU (measured 20% faster at 4096 -> 11008; slower where the grid fits)
+    // so one workgroup fits a CU; with more row blocks than CUs (but too few for two blocks per
+    // workgroup), four-wave workgroups (half the LDS) let two share a CU (measured 20% faster at
+    // 4096 -> 11008 with one block per workgroup; slower where the grid fits)
     if constexpr (FMT == TRI_FMT_1P6BIT && MT == 16) {
-        if (!glue_bits(fu) && gr.blk[gr.G] > kCUs) {
+        if (!glue_bits(fu) && rb == 1 && (int64_t)gr.blk[gr.G] * ((M + 15) / 16) > kCUs) {
             switch ((C + 15) / 16) {
             case 1: return launch_cfg<FMT, MT, 4, 1>(X, gr, M, K, C, s, fu);
             case 2: return launch_cfg<FMT, MT, 4, 2>(X, gr, M, K, C, s, fu);
@@ -335,14 +402,14 @@ static bool launch_mt(const uint16_t *X, const Groups &gr, int M, int K, int C, 
     }
     const int cst8 = (C + 31) / 32;              // chunk-steps with 8 waves (4 chunks per step and wave)
     switch (cst8) {
-    case 1: return launch_cfg<FMT, MT, 8, 1>(X, gr, M, K, C, s, fu);
-    case 2: return launch_cfg<FMT, MT, 8, 2>(X, gr, M, K, C, s, fu);
-    case 3: return launch_cfg<FMT, MT, 8, 3>(X, gr, M, K, C, s, fu);
-    case 4: return launch_cfg<FMT, MT, 8, 4>(X, gr, M, K, C, s, fu);
-    case 5: return launch_cfg<FMT, MT, 8, 5>(X, gr, M, K, C, s, fu);
-    case 6: return launch_cfg<FMT, MT, 8, 6>(X, gr, M, K, C, s, fu);
-    case 7: return launch_cfg<FMT, MT, 8, 7>(X, gr, M, K, C, s, fu);
-    case 8: return launch_cfg<FMT, MT, 8, 8>(X, gr, M, K, C, s, fu);
+    case 1: return launch_cfg<FMT, MT, 8, 1>(X, gr, M, K, C, s, fu, rb);
+    case 2: return launch_cfg<FMT, MT, 8, 2>(X, gr, M, K, C, s, fu, rb);
+    case 3: return launch_cfg<FMT, MT, 8, 3>(X, gr, M, K, C, s, fu, rb);
+    case 4: return launch_cfg<FMT, MT, 8, 4>(X, gr, M, K, C, s, fu, rb);
+    case 5: return launch_cfg<FMT, MT, 8, 5>(X, gr, M, K, C, s, fu, rb);
+    case 6: return launch_cfg<FMT, MT, 8, 6>(X, gr, M, K, C, s, fu, rb);
+    case 7: return launch_cfg<FMT, MT, 8, 7>(X, gr, M, K, C, s, fu, rb);
+    case 8: return launch_cfg<FMT, MT, 8, 8>(X, gr, M, K, C, s, fu, rb);
     default: break;
     }
     // sixteen waves, while the per-wave activation slots fit in LDS (the norm and pair variants
@@ -359,19 +426,22 @@ static bool launch_mt(const uint16_t *X, const Groups &gr, int M, int K, int C, 
 bool launch_mvm(const uint16_t *X, const Groups &gr, int M, int K, int fmt, hipStream_t s, const Fusion *fu)
 {
     const int C = (int)(row_bytes(K, fmt) / 16);
-    // 32-bit buffer offsets: the activations and one 16-row block stay below 2^31 bytes;
-    // activations are read in pieces of 8 values, so K must be a multiple of 8
-    if (M < 2 || M > 16 || (K % 8) != 0 || (int64_t)M * K * 2 >= ((int64_t)1 << 31) ||
+    // 32-bit buffer offsets: one 16-row slice of the activations and one 16-row block of the
+    // weights stay below 2^31 bytes; activations are read in pieces of 8 values, so K must be a
+    // multiple of 8.  More than 16 rows run as 16-row slices (the second grid dimension).
+    if (M < 2 || M > 16 * 65535 || (K % 8) != 0 || 16 * (int64_t)K * 2 >= ((int64_t)1 << 31) ||
         16 * (int64_t)C * 16 >= ((int64_t)1 << 31))
         return false;
+    if (M > 16 && fu) return false;              // the block glue serves up to 16 rows
+    const int rb = glue_bits(fu) ? 1 : choose_rb(gr, M);
     if (fmt == TRI_FMT_2BIT) {
-        if (M <= 4) return launch_mt<TRI_FMT_2BIT, 4>(X, gr, M, K, C, s, fu);
-        if (M <= 8) return launch_mt<TRI_FMT_2BIT, 8>(X, gr, M, K, C, s, fu);
-        return launch_mt<TRI_FMT_2BIT, 16>(X, gr, M, K, C, s, fu);
+        if (M <= 4) return launch_mt<TRI_FMT_2BIT, 4>(X, gr, M, K, C, s, fu, rb);
+        if (M <= 8) return launch_mt<TRI_FMT_2BIT, 8>(X, gr, M, K, C, s, fu, rb);
+        return launch_mt<TRI_FMT_2BIT, 16>(X, gr, M, K, C, s, fu, rb);
     }
-    if (M <= 4) return launch_mt<TRI_FMT_1P6BIT, 4>(X, gr, M, K, C, s, fu);
-    if (M <= 8) return launch_mt<TRI_FMT_1P6BIT, 8>(X, gr, M, K, C, s, fu);
-    return launch_mt<TRI_FMT_1P6BIT, 16>(X, gr, M, K, C, s, fu);
+    if (M <= 4) return launch_mt<TRI_FMT_1P6BIT, 4>(X, gr, M, K, C, s, fu, rb);
+    if (M <= 8) return launch_mt<TRI_FMT_1P6BIT, 8>(X, gr, M, K, C, s, fu, rb);
+    return launch_mt<TRI_FMT_1P6BIT, 16>(X, gr, M, K, C, s, fu, rb);
 }
 
 }  // namespace tri

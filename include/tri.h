@@ -53,8 +53,10 @@ enum {
 enum {
     TRI_ALGO_AUTO = 0,     /* pick from (M, fmt): the default of tri_linear */
     TRI_ALGO_GEMV = 1,     /* M == 1, 2-bit only: VALU dot products, lanes own K-slices */
-    TRI_ALGO_SMALLM = 2,   /* 1 <= M <= 16: MFMA 16x16x32 f16 with trits decoded in registers
-                              (also the choice at M = 1, where it outruns the VALU kernel) */
+    TRI_ALGO_SMALLM = 2,   /* any M, in 16-row slices of X: MFMA 16x16x32 f16 with trits decoded
+                              in registers, one pass over the weights per slice (the choice up to
+                              M = 16, M = 1 included, and above while the GEMM has too few tiles
+                              to fill the chip) */
     TRI_ALGO_GEMM = 3      /* any M: tiled MFMA 32x32x16 f16 GEMM, activations staged in LDS and
                               trits decoded in registers (prefill) */
 };
@@ -119,8 +121,7 @@ int tri_linear(const _Float16 *X, const uint8_t *Wp, float scale,
                int64_t M, int64_t N, int64_t K, int fmt, _Float16 *Y, hipStream_t stream);
 
 /* tri_linear with the kernel family chosen by the caller (for measurement and
- * tests).  TRI_ALGO_GEMV needs M == 1 and TRI_FMT_2BIT; TRI_ALGO_SMALLM needs
- * M <= 16; otherwise TRI_EINVAL.  Results of every family satisfy the same
+ * tests).  TRI_ALGO_GEMV needs M == 1 and TRI_FMT_2BIT, else TRI_EINVAL.  Results of every family satisfy the same
  * error bound; they are not bitwise equal to one another. */
 int tri_linear_algo(const _Float16 *X, const uint8_t *Wp, float scale,
                     int64_t M, int64_t N, int64_t K, int fmt, _Float16 *Y,
@@ -131,8 +132,9 @@ int tri_linear_algo(const _Float16 *X, const uint8_t *Wp, float scale,
  * g < G,  Y[g] = fp16_rne(scale[g] * X W_g^T)  with W_g of N[g] rows packed for this K and
  * fmt, exactly as tri_linear would compute each one.  Wp, scale, N and Y are HOST arrays of
  * G entries (the pointers they hold are device pointers, with tri_linear's alignment and
- * aliasing rules); 1 <= G <= TRI_MAX_GROUPS.  For M <= 16 one launch serves all G matrices
- * (the launch's fixed cost is paid once); other shapes run one launch per matrix.
+ * aliasing rules); 1 <= G <= TRI_MAX_GROUPS.  Where tri_linear would pick TRI_ALGO_SMALLM for
+ * every matrix, one launch serves all G (the launch's fixed cost is paid once); other shapes
+ * run one call per matrix.
  * Errors: those of tri_linear for any matrix, TRI_EINVAL for a bad G or a null array. */
 enum { TRI_MAX_GROUPS = 4 };
 int tri_linear_grouped(const _Float16 *X, const uint8_t *const *Wp, const float *scale, int64_t M,
@@ -176,7 +178,10 @@ int tri_linear_fused(const _Float16 *X, const uint8_t *const *Wp, const float *s
                      const int64_t *N, int64_t K, int fmt, _Float16 *const *Y, int G,
                      const tri_glue *glue, hipStream_t stream);
 
-/* The algorithm tri_linear would pick for (M, N, K, fmt); TRI_EINVAL if invalid. */
+/* The algorithm tri_linear would pick for (M, N, K, fmt); TRI_EINVAL if invalid.  Up to
+ * M = 16 it is TRI_ALGO_SMALLM; above, whichever of TRI_ALGO_SMALLM and TRI_ALGO_GEMM a cost
+ * model fitted to MI355X timings says is faster (the small-M kernels' time grows with the
+ * number of 16-row slices, the GEMM's with its rounds of 128 x 512 tiles). */
 int tri_select_algo(int64_t M, int64_t N, int64_t K, int fmt);
 
 /* Human-readable name of a status code (static string, never NULL). */

@@ -25,9 +25,7 @@ def host(t):
 
 def algos_for(M, fmt):
     """Kernel families that can serve (M, fmt)."""
-    out = [tri.TRI_ALGO_GEMM]
-    if M <= 16:
-        out.append(tri.TRI_ALGO_SMALLM)
+    out = [tri.TRI_ALGO_GEMM, tri.TRI_ALGO_SMALLM]
     if M == 1 and fmt == tri.TRI_FMT_2BIT:
         out.append(tri.TRI_ALGO_GEMV)
     return out

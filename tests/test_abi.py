@@ -50,7 +50,20 @@ def test_select_algo():
     assert tri.tri_select_algo(1, 4096, 4096, F2) == tri.TRI_ALGO_SMALLM   # the MFMA kernel also serves M = 1
     assert tri.tri_select_algo(1, 4096, 4096, F16) == tri.TRI_ALGO_SMALLM
     assert tri.tri_select_algo(16, 4096, 4096, F2) == tri.TRI_ALGO_SMALLM
-    assert tri.tri_select_algo(17, 4096, 4096, F2) == tri.TRI_ALGO_GEMM
+    # above 16 rows, the cheaper of the two by the fitted cost model (crossovers measured on MI355X)
+    assert tri.tri_select_algo(17, 4096, 4096, F2) == tri.TRI_ALGO_SMALLM
+    assert tri.tri_select_algo(384, 4096, 4096, F2) == tri.TRI_ALGO_SMALLM
+    assert tri.tri_select_algo(512, 4096, 4096, F2) == tri.TRI_ALGO_GEMM
+    assert tri.tri_select_algo(128, 11008, 4096, F2) == tri.TRI_ALGO_SMALLM
+    assert tri.tri_select_algo(192, 11008, 4096, F2) == tri.TRI_ALGO_GEMM
+    assert tri.tri_select_algo(48, 28672, 8192, F2) == tri.TRI_ALGO_SMALLM
+    assert tri.tri_select_algo(64, 28672, 8192, F2) == tri.TRI_ALGO_GEMM
+    assert tri.tri_select_algo(32, 8192, 28672, F2) == tri.TRI_ALGO_SMALLM    # rows past the eight-wave kernels
+    assert tri.tri_select_algo(48, 8192, 28672, F2) == tri.TRI_ALGO_GEMM
+    assert tri.tri_select_algo(64, 8192, 28672, F16) == tri.TRI_ALGO_SMALLM
+    assert tri.tri_select_algo(96, 8192, 28672, F16) == tri.TRI_ALGO_GEMM
+    assert tri.tri_select_algo(2048, 28672, 8192, F2) == tri.TRI_ALGO_GEMM
+    assert tri.tri_select_algo(2048, 8192, 28672, F16) == tri.TRI_ALGO_GEMM
     assert tri.tri_select_algo(0, 4096, 4096, F2) == tri.TRI_EINVAL
     assert tri.tri_select_algo(1, 4096, 4096, 3) == tri.TRI_EINVAL
 
@@ -78,7 +91,6 @@ def test_linear_argument_errors_launch_nothing():
     # a kernel family that cannot serve the shape
     assert raw("tri_linear_algo", A, B, 1.0, 2, 4, 64, F2, C, tri.TRI_ALGO_GEMV, s) == tri.TRI_EINVAL
     assert raw("tri_linear_algo", A, B, 1.0, 1, 4, 64, tri.TRI_FMT_1P6BIT, C, tri.TRI_ALGO_GEMV, s) == tri.TRI_EINVAL
-    assert raw("tri_linear_algo", A, B, 1.0, 17, 4, 64, F2, C, tri.TRI_ALGO_SMALLM, s) == tri.TRI_EINVAL
     assert raw("tri_linear_algo", A, B, 1.0, 1, 4, 64, F2, C, 9, s) == tri.TRI_EINVAL
 
 

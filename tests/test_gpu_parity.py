@@ -87,7 +87,10 @@ RAGGED = [(1, 1, 1), (1, 37, 1000), (1, 130, 4097), (1, 300, 81), (1, 33, 12000)
           (5, 300, 81), (16, 50, 4097), (16, 1, 160), (7, 1025, 640), (17, 40, 200), (40, 70, 700),
           (64, 96, 513), (130, 257, 1111), (129, 300, 1000), (200, 513, 2048), (256, 260, 328),
           (150, 100, 64), (96, 600, 320), (33, 700, 1088),
-          (13, 4200, 1000), (16, 4111, 2000), (12, 4500, 4096)]   # > 256 row blocks of 16 rows
+          (13, 4200, 1000), (16, 4111, 2000), (12, 4500, 4096),   # > 256 row blocks of 16 rows
+          # workgroups of two and four 16-row blocks (grids of >= 160 such workgroups), ragged ends
+          (9, 5200, 2000), (3, 11000, 640), (6, 10250, 1000), (16, 10250, 512), (40, 4100, 1000),
+          (33, 5150, 4096)]
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -325,9 +328,10 @@ def test_gemm_full_tiles_ragged_edges(fmt):
     say("  worst err/tol %.3g, fraction equal to fp16(ref) %.3f" % (worst, exact))
 
 
-# Grouped layers: several matrices reading the same activations, one launch for M <= 16
-# (K = 1000: the grouped kernels; K = 1001: one launch per matrix).
-GROUPED = [(1, 1000), (3, 1000), (16, 1000), (1, 1001), (5, 1001), (20, 1000)]
+# Grouped layers: several matrices reading the same activations, one launch where the small-M
+# kernels serve every matrix (K = 1000: the grouped kernels, also over 16-row slices for M > 16;
+# K = 1001: one launch per matrix).
+GROUPED = [(1, 1000), (3, 1000), (16, 1000), (1, 1001), (5, 1001), (20, 1000), (40, 1000), (20, 1001)]
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -348,4 +352,26 @@ def test_grouped_layers(fmt, case):
         Yh = host(Y)
         check_layer(Yh, X, W, s, "grouped M=%d K=%d fmt=%d g=%d" % (M, K, fmt, g))
         # the same kernels as a single layer: identical results
+        np.testing.assert_array_equal(Yh, host(tri.linear(Xd, Wps[g], s, K, fmt)))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M", [8, 16, 24])
+def test_grouped_large_grid_same_as_single(fmt, M):
+    """Q, K, V-like projections (3 x 4096 rows): the grouped grid is large enough for workgroups of
+    several 16-row blocks while each single layer's is not; the results are bitwise the same."""
+    import torch
+    K = 1000
+    Ns = [4096, 4096, 4096]
+    X = synth.activations(synth.rng_for(410 + fmt, M, synth.STREAM_X), M, K)
+    Ws = [synth.trits(synth.rng_for(410 + fmt, 10 * M + g, synth.STREAM_W), n, K) for g, n in enumerate(Ns)]
+    scales = [0.02, -0.03, 0.045]
+    Xd = cuda(X)
+    Wps = [tri.pack(cuda(W), fmt) for W in Ws]
+    Ys = [torch.empty((M, n), dtype=torch.float16, device="cuda") for n in Ns]
+    say("grouped 3x4096 M=%d K=%d fmt=%d" % (M, K, fmt))
+    tri.tri_linear_grouped(Xd, Wps, scales, M, Ns, K, fmt, Ys)
+    for g, (W, s, Y) in enumerate(zip(Ws, scales, Ys)):
+        Yh = host(Y)
+        check_layer(Yh, X, W, s, "grouped 3x4096 M=%d fmt=%d g=%d" % (M, fmt, g))
         np.testing.assert_array_equal(Yh, host(tri.linear(Xd, Wps[g], s, K, fmt)))
