@@ -61,7 +61,7 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
 {
     constexpr bool NORM = (GL & kGlueNorm) != 0;
     constexpr bool PAIR = (GL & kGluePair) != 0;
-    static_assert(GL == 0 || RB == 1, "the glue variants own one 16-row block per workgroup");
+    static_assert(!PAIR || RB == 1, "the pair variant owns one 16-row block of each matrix per workgroup");
     const int gi = group_of(gr, (int)blockIdx.x);
     const uint8_t *__restrict__ Wp = gr.Wp[gi];
     const float scale = gr.scale[gi];
@@ -316,13 +316,15 @@ constexpr bool has_glue()
 
 // Several 16-row blocks per workgroup (RB): every activation value a wave reads feeds RB
 // blocks, so the activations are re-read from cache RB times less often.  Variants exist for
-// eight waves without glue, and only where the weight registers do not spill.
-template <int FMT, int MT, int CST, int RB>
+// eight waves, without glue or with the norm, and only where the registers do not spill.
+template <int FMT, int MT, int CST, int RB, int GL>
 constexpr bool has_rb()
 {
     if (RB == 1) return true;
-    if (RB == 2) return FMT == TRI_FMT_2BIT ? CST <= 8 : (MT == 16 ? CST <= 5 : CST <= 6);
-    if (RB == 4) return FMT == TRI_FMT_2BIT && (MT == 16 ? CST <= 3 : MT == 8 ? CST <= 4 : CST <= 5);
+    if (GL & kGluePair) return false;
+    const int c = CST + ((GL & kGlueNorm) ? 1 : 0);   // the norm takes about one more step's registers
+    if (RB == 2) return FMT == TRI_FMT_2BIT ? (MT == 16 ? c <= 6 : c <= 8) : (MT == 16 ? c <= 5 : c <= 6);
+    if (RB == 4) return FMT == TRI_FMT_2BIT && (MT == 16 ? c <= 3 : MT == 8 ? c <= 4 : c <= 5);
     return false;
 }
 
@@ -350,7 +352,7 @@ int choose_rb(const Groups &gr, int M)
 template <int FMT, int MT, int NW, int CST, int GL, int RB>
 static bool launch_gl(const uint16_t *X, const Groups &gr, int M, int K, int C, hipStream_t s, const Fusion &f)
 {
-    if constexpr (has_glue<FMT, MT, NW, CST, GL>() && has_rb<FMT, MT, CST, RB>()) {
+    if constexpr (has_glue<FMT, MT, NW, CST, GL>() && has_rb<FMT, MT, CST, RB, GL>()) {
         const Groups g = RB == 1 ? gr : regroup(gr, RB);
         hipLaunchKernelGGL((k_mvm<FMT, MT, NW, CST, GL, RB>), dim3(g.blk[g.G], (M + 15) / 16), dim3(64 * NW), 0, s, X,
                            g, M, K, C, f);
@@ -365,11 +367,16 @@ static bool launch_cfg(const uint16_t *X, const Groups &gr, int M, int K, int C,
 {
     const Fusion f = fu ? *fu : Fusion{};
     switch (glue_bits(fu)) {
-    case kGlueNorm: return launch_gl<FMT, MT, NW, CST, kGlueNorm, 1>(X, gr, M, K, C, s, f);
+    case kGlueNorm:
+        if constexpr (NW == 8) {                 // the largest RB up to rb that has a variant
+            if (rb >= 4 && launch_gl<FMT, MT, NW, CST, kGlueNorm, 4>(X, gr, M, K, C, s, f)) return true;
+            if (rb >= 2 && launch_gl<FMT, MT, NW, CST, kGlueNorm, 2>(X, gr, M, K, C, s, f)) return true;
+        }
+        return launch_gl<FMT, MT, NW, CST, kGlueNorm, 1>(X, gr, M, K, C, s, f);
     case kGluePair: return launch_gl<FMT, MT, NW, CST, kGluePair, 1>(X, gr, M, K, C, s, f);
     case kGlueNorm | kGluePair: return launch_gl<FMT, MT, NW, CST, kGlueNorm | kGluePair, 1>(X, gr, M, K, C, s, f);
     default:
-        if constexpr (NW == 8) {                 // the largest RB up to rb that has a variant
+        if constexpr (NW == 8) {
             if (rb >= 4 && launch_gl<FMT, MT, NW, CST, 0, 4>(X, gr, M, K, C, s, f)) return true;
             if (rb >= 2 && launch_gl<FMT, MT, NW, CST, 0, 2>(X, gr, M, K, C, s, f)) return true;
         }
@@ -433,7 +440,7 @@ bool launch_mvm(const uint16_t *X, const Groups &gr, int M, int K, int fmt, hipS
         16 * (int64_t)C * 16 >= ((int64_t)1 << 31))
         return false;
     if (M > 16 && fu) return false;              // the block glue serves up to 16 rows
-    const int rb = glue_bits(fu) ? 1 : choose_rb(gr, M);
+    const int rb = (glue_bits(fu) & kGluePair) ? 1 : choose_rb(gr, M);
     if (fmt == TRI_FMT_2BIT) {
         if (M <= 4) return launch_mt<TRI_FMT_2BIT, 4>(X, gr, M, K, C, s, fu, rb);
         if (M <= 8) return launch_mt<TRI_FMT_2BIT, 8>(X, gr, M, K, C, s, fu, rb);

@@ -146,6 +146,23 @@ def test_fused_silu_pair(fmt, shape):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M", [4, 8, 16])
+def test_fused_norm_multi_block_workgroups(fmt, M):
+    """Grids large enough for workgroups of several 16-row blocks (4096 + 4096 + 2000 rows): the
+    norm variant with the gain and a residual, ragged last block."""
+    K = 1000
+    Ns = [4096, 4096, 2000]
+    Ws, scales, X, gain, Rs = inputs(M, K, Ns, 985)
+    Wps = [tri.pack(cuda(W), fmt) for W in Ws]
+    Ys = run_fused(X, Wps, scales, Ns, K, fmt, norm=True, gain=gain, Rs=Rs)
+    worst = 0.0
+    for g in range(len(Ns)):
+        worst = max(worst, check_layer_fused(Ys[g], X, Ws[g], scales[g], True, gain, 1e-5, Rs[g],
+                                             "multi-block M=%d fmt=%d matrix %d" % (M, fmt, g)))
+    say("multi-block norm M=%d fmt=%d: worst error / tolerance %.3f" % (M, fmt, worst))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 def test_fused_without_glue_equals_grouped_bitwise(fmt):
     import torch
     for (M, K) in [(1, 4096), (5, 1000), (16, 11008)]:
