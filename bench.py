@@ -299,6 +299,7 @@ def main():
     if not args.skip_extra:
         out["decode_1p6bit"] = bench_decode_1p6(clock)
         out["batched"] = bench_batched(clock)
+        out["mid_m"] = bench_mid_m(clock)
         out["block"] = bench_block(clock)
         out["prefill"] = bench_prefill(clock)
         out["quantize"] = bench_quantize(clock)
@@ -321,6 +322,26 @@ def bench_batched(clock):
                             "GBps": round(L.bytes / t / 1e9, 1), "frac_hbm": round(L.bytes / t / 1e9 / HBM_PEAK_GBS, 4)})
                 del L
                 torch.cuda.empty_cache()
+    return res
+
+
+def bench_mid_m(clock):
+    """16 < M <= 256 with cold weights, on the kernel family tri_linear picks for the shape."""
+    import torch
+    import bit_mixed_precision_tri_amd as tri
+    from bit_mixed_precision_tri_amd import configs
+    cfg = configs.MID_M
+    res = []
+    for li, (name, K, N) in enumerate(cfg["shapes"]):
+        for M in cfg["Ms"]:
+            L = Layer(cfg["workload_id"], 10 * li + M, M, N, K, cfg["fmt"], copies=16)
+            t, _ = clock.run([L.launch] * 50)
+            res.append({"shape": name, "M": M, "format": configs.FMT_NAMES[cfg["fmt"]],
+                        "algo": tri.ALGO_NAMES[tri.tri_select_algo(M, N, K, cfg["fmt"])],
+                        "kernel_us": round(t * 1e6, 3), "GBps": round(L.bytes / t / 1e9, 1),
+                        "TFLOPs": round(L.flops / t / 1e12, 2)})
+            del L
+            torch.cuda.empty_cache()
     return res
 
 

@@ -24,6 +24,11 @@ BATCHED = dict(workload_id=3, Ms=(4, 8, 16),
                shapes=[("gate_up_4096to11008", 4096, 11008), ("down_11008to4096", 11008, 4096)],
                fmts=(FMT_2BIT, FMT_1P6BIT))
 
+# workload 6: a middling number of rows (large-batch decode, short prefill chunks), 2-bit, on the
+# kernel family tri_linear picks (the small-M kernels over 16-row slices, or the GEMM)
+MID_M = dict(workload_id=6, Ms=(32, 64, 128, 256),
+             shapes=[("gate_up_4096to11008", 4096, 11008), ("down_11008to4096", 11008, 4096)], fmt=FMT_2BIT)
+
 # workload 4: one LLaMA-style block decode step (seven ternary linears), M in {1, 8}
 BLOCK_LAYERS = [  # (name, K, N)
     ("q", 4096, 4096), ("k", 4096, 4096), ("v", 4096, 4096), ("o", 4096, 4096),

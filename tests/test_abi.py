@@ -52,16 +52,17 @@ def test_select_algo():
     assert tri.tri_select_algo(16, 4096, 4096, F2) == tri.TRI_ALGO_SMALLM
     # above 16 rows, the cheaper of the two by the fitted cost model (crossovers measured on MI355X)
     assert tri.tri_select_algo(17, 4096, 4096, F2) == tri.TRI_ALGO_SMALLM
-    assert tri.tri_select_algo(384, 4096, 4096, F2) == tri.TRI_ALGO_SMALLM
-    assert tri.tri_select_algo(512, 4096, 4096, F2) == tri.TRI_ALGO_GEMM
-    assert tri.tri_select_algo(128, 11008, 4096, F2) == tri.TRI_ALGO_SMALLM
-    assert tri.tri_select_algo(192, 11008, 4096, F2) == tri.TRI_ALGO_GEMM
-    assert tri.tri_select_algo(48, 28672, 8192, F2) == tri.TRI_ALGO_SMALLM
-    assert tri.tri_select_algo(64, 28672, 8192, F2) == tri.TRI_ALGO_GEMM
-    assert tri.tri_select_algo(32, 8192, 28672, F2) == tri.TRI_ALGO_SMALLM    # rows past the eight-wave kernels
-    assert tri.tri_select_algo(48, 8192, 28672, F2) == tri.TRI_ALGO_GEMM
-    assert tri.tri_select_algo(64, 8192, 28672, F16) == tri.TRI_ALGO_SMALLM
-    assert tri.tri_select_algo(96, 8192, 28672, F16) == tri.TRI_ALGO_GEMM
+    assert tri.tri_select_algo(256, 4096, 4096, F2) == tri.TRI_ALGO_SMALLM
+    assert tri.tri_select_algo(384, 4096, 4096, F2) == tri.TRI_ALGO_GEMM
+    assert tri.tri_select_algo(96, 11008, 4096, F2) == tri.TRI_ALGO_SMALLM
+    assert tri.tri_select_algo(128, 11008, 4096, F2) == tri.TRI_ALGO_GEMM
+    assert tri.tri_select_algo(256, 4096, 11008, F2) == tri.TRI_ALGO_SMALLM
+    assert tri.tri_select_algo(384, 4096, 11008, F2) == tri.TRI_ALGO_GEMM
+    assert tri.tri_select_algo(32, 28672, 8192, F2) == tri.TRI_ALGO_SMALLM
+    assert tri.tri_select_algo(48, 28672, 8192, F2) == tri.TRI_ALGO_GEMM
+    assert tri.tri_select_algo(32, 8192, 28672, F2) == tri.TRI_ALGO_GEMM     # rows past the eight-wave kernels
+    assert tri.tri_select_algo(48, 8192, 28672, F16) == tri.TRI_ALGO_SMALLM
+    assert tri.tri_select_algo(64, 8192, 28672, F16) == tri.TRI_ALGO_GEMM
     assert tri.tri_select_algo(2048, 28672, 8192, F2) == tri.TRI_ALGO_GEMM
     assert tri.tri_select_algo(2048, 8192, 28672, F16) == tri.TRI_ALGO_GEMM
     assert tri.tri_select_algo(0, 4096, 4096, F2) == tri.TRI_EINVAL

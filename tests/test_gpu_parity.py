@@ -90,7 +90,9 @@ RAGGED = [(1, 1, 1), (1, 37, 1000), (1, 130, 4097), (1, 300, 81), (1, 33, 12000)
           (13, 4200, 1000), (16, 4111, 2000), (12, 4500, 4096),   # > 256 row blocks of 16 rows
           # workgroups of two and four 16-row blocks (grids of >= 160 such workgroups), ragged ends
           (9, 5200, 2000), (3, 11000, 640), (6, 10250, 1000), (16, 10250, 512), (40, 4100, 1000),
-          (33, 5150, 4096)]
+          (33, 5150, 4096),
+          # a middling M: the GEMM on quarter-width tiles (at most 64 tiles) and on half-width ones
+          (100, 11000, 1000), (300, 16001, 72)]
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -248,6 +250,21 @@ def test_batched_decode_full_size(fmt):
             say("batched %s M=%d fmt=%d" % (name, M, fmt))
             worst, exact = check_layer(run_layer(X, Wp, s, K, fmt, tri.TRI_ALGO_AUTO), X, W, s,
                                        "batched %s M=%d fmt=%d" % (name, M, fmt))
+            say("  worst err/tol %.3g, fraction equal to fp16(ref) %.3f" % (worst, exact))
+
+
+def test_mid_m_workload_sampled_rows():
+    """The middling-M workload as bench.py times it (same inputs, the kernel family tri_linear
+    picks): sampled rows, including both sides of every 16-row slice boundary the rows cross."""
+    cfg = configs.MID_M
+    fmt = cfg["fmt"]
+    for li, (name, K, N) in enumerate(cfg["shapes"]):
+        for M in cfg["Ms"]:
+            W, X, s = synth.layer_inputs(cfg["workload_id"], 10 * li + M, M, N, K)
+            rows = sorted({0, 1, 15, 16, 17, M // 2, M - 17, M - 16, M - 1})
+            say("mid-M %s M=%d algo=%s" % (name, M, tri.ALGO_NAMES[tri.tri_select_algo(M, N, K, fmt)]))
+            Y = run_layer(X, tri.pack(cuda(W), fmt), s, K, fmt, tri.TRI_ALGO_AUTO)
+            worst, exact = check_layer(Y, X, W, s, "mid-M %s M=%d" % (name, M), rows=rows)
             say("  worst err/tol %.3g, fraction equal to fp16(ref) %.3f" % (worst, exact))
 
 
