@@ -33,7 +33,8 @@ int check_linear(const void *X, const void *Wp, int64_t M, int64_t N, int64_t K,
 // (M = 17 .. 512; K x N = 4096 x 4096, 4096 x 11008, 11008 x 4096, 8192 x 28672, 28672 x 8192;
 // both formats):
 //   small-M  ceil(M/16) * N * c,  c = 0.10 ps (2-bit) / 0.15 ps (1.6-bit) per trit and slice;
-//            rows too long for the eight-wave kernels run 5x / 1.9x slower;
+//            rows past eight steps per wave 1.6x / 1.2x that, rows past sixteen (the streaming
+//            kernel) 5x / 1.9x;
 //   GEMM     T = ceil(M/128) * ceil(N/512) tiles; at most 64: one round of quarter-width
 //            tiles, 8 ns (2-bit) / 9 ns (1.6-bit); else u * R, u = 11 ns / 13.3 ns per round
 //            of half-width tiles, R = the rounds of its launch (a last round of at most 128
@@ -43,7 +44,8 @@ int select_algo(int64_t M, int64_t N, int64_t K, int fmt)
     if (M <= 16) return TRI_ALGO_SMALLM;
     const bool two = fmt == TRI_FMT_2BIT;
     double c = two ? 0.10 : 0.15;                // ps
-    if (K > (two ? 16384 : 20480)) c *= two ? 5.0 : 1.9;
+    if (K > (two ? 32768 : 35840)) c *= two ? 5.0 : 1.9;
+    else if (K > (two ? 16384 : 20480)) c *= two ? 1.6 : 1.2;
     const int64_t T = ((M + 127) / 128) * ((N + 511) / 512);
     const int64_t r = T % kCUs;
     const int64_t R = (r > 0 && r <= kCUs / 2) ? 2 * (T / kCUs) + 1 : 2 * ((T + kCUs - 1) / kCUs);

@@ -301,14 +301,13 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
     }
 }
 
-// Glue variants that exist: eight waves only (the slots of sixteen, one row longer, overflow
-// LDS), and none whose registers would overflow (1.6-bit tiles of 16 rows past 6 steps; pairs
-// of 16-row tiles past 4 steps).
+// Glue variants that exist: eight waves and up to eight steps only, and none whose registers
+// would overflow (1.6-bit tiles of 16 rows past 6 steps; pairs of 16-row tiles past 4 steps).
 template <int FMT, int MT, int NW, int CST, int GL>
 constexpr bool has_glue()
 {
     if (GL == 0) return true;
-    if (NW != 8) return false;
+    if (NW != 8 || CST > 8) return false;
     if ((GL & kGlueNorm) && FMT == TRI_FMT_1P6BIT && MT == 16 && CST > 6) return false;
     if ((GL & kGluePair) && MT == 16 && CST > 4) return false;
     return true;
@@ -419,13 +418,19 @@ static bool launch_mt(const uint16_t *X, const Groups &gr, int M, int K, int C, 
     case 8: return launch_cfg<FMT, MT, 8, 8>(X, gr, M, K, C, s, fu, rb);
     default: break;
     }
-    // sixteen waves, while the per-wave activation slots fit in LDS (the norm and pair variants
-    // stay at eight waves)
-    if (glue_bits(fu)) return false;
-    if constexpr (FMT == TRI_FMT_2BIT || MT <= 8) {
-        const int cst16 = (C + 63) / 64;
-        if (cst16 <= 8) return launch_cfg<FMT, MT, 16, 8>(X, gr, M, K, C, s, fu);
-        if (cst16 <= 16) return launch_cfg<FMT, MT, 16, 16>(X, gr, M, K, C, s, fu);
+    // longer rows (up to 16 steps): eight waves still, one block per workgroup and no glue.  (A
+    // sixteen-wave workgroup has 128 registers per lane, too few for these steps: its variants
+    // spilled and ran 1.2-3.5x slower.)
+    if (!glue_bits(fu)) {
+        switch (cst8) {
+        case 9: case 10: return launch_cfg<FMT, MT, 8, 10>(X, gr, M, K, C, s, fu, 1);
+        case 11: case 12: return launch_cfg<FMT, MT, 8, 12>(X, gr, M, K, C, s, fu, 1);
+        case 13: case 14: return launch_cfg<FMT, MT, 8, 14>(X, gr, M, K, C, s, fu, 1);
+        case 15: case 16:
+            if constexpr (FMT == TRI_FMT_2BIT || MT <= 8) return launch_cfg<FMT, MT, 8, 16>(X, gr, M, K, C, s, fu, 1);
+            break;
+        default: break;
+        }
     }
     return false;                                // longer rows: the streaming small-M kernel
 }

@@ -60,9 +60,10 @@ def test_select_algo():
     assert tri.tri_select_algo(384, 4096, 11008, F2) == tri.TRI_ALGO_GEMM
     assert tri.tri_select_algo(32, 28672, 8192, F2) == tri.TRI_ALGO_SMALLM
     assert tri.tri_select_algo(48, 28672, 8192, F2) == tri.TRI_ALGO_GEMM
-    assert tri.tri_select_algo(32, 8192, 28672, F2) == tri.TRI_ALGO_GEMM     # rows past the eight-wave kernels
-    assert tri.tri_select_algo(48, 8192, 28672, F16) == tri.TRI_ALGO_SMALLM
-    assert tri.tri_select_algo(64, 8192, 28672, F16) == tri.TRI_ALGO_GEMM
+    assert tri.tri_select_algo(64, 8192, 28672, F2) == tri.TRI_ALGO_SMALLM    # rows past eight steps per wave
+    assert tri.tri_select_algo(128, 8192, 28672, F2) == tri.TRI_ALGO_GEMM
+    assert tri.tri_select_algo(64, 8192, 28672, F16) == tri.TRI_ALGO_SMALLM
+    assert tri.tri_select_algo(128, 8192, 28672, F16) == tri.TRI_ALGO_GEMM
     assert tri.tri_select_algo(2048, 28672, 8192, F2) == tri.TRI_ALGO_GEMM
     assert tri.tri_select_algo(2048, 8192, 28672, F16) == tri.TRI_ALGO_GEMM
     assert tri.tri_select_algo(0, 4096, 4096, F2) == tri.TRI_EINVAL

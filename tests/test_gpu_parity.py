@@ -92,7 +92,9 @@ RAGGED = [(1, 1, 1), (1, 37, 1000), (1, 130, 4097), (1, 300, 81), (1, 33, 12000)
           (9, 5200, 2000), (3, 11000, 640), (6, 10250, 1000), (16, 10250, 512), (40, 4100, 1000),
           (33, 5150, 4096),
           # a middling M: the GEMM on quarter-width tiles (at most 64 tiles) and on half-width ones
-          (100, 11000, 1000), (300, 16001, 72)]
+          (100, 11000, 1000), (300, 16001, 72),
+          # long rows: 9..16 steps per wave of eight (2-bit and 1.6-bit), and past that the streaming kernel
+          (5, 300, 24000), (16, 200, 30000), (8, 100, 40000), (12, 100, 40000), (20, 90, 26000)]
 
 
 @pytest.mark.parametrize("fmt", FMTS)
