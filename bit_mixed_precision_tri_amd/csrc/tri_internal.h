@@ -71,14 +71,28 @@ inline int glue_bits(const Fusion *fu)
     return fu ? (fu->norm ? kGlueNorm : 0) | (fu->pair ? kGluePair : 0) : 0;
 }
 
-// The matrix of a grouped launch that a workgroup (by its 16-row block) belongs to.
-__device__ __forceinline__ int group_of(const Groups &gr, int block)
+// The matrix of a grouped launch that a workgroup (by its block index) belongs to, with its
+// fields.  ONE (a launch for one matrix) makes every field a constant-offset kernel argument;
+// the kernels' single-matrix variants are measurably faster at the start of a short decode
+// launch (0.2-0.35 us of 3-5 us, with the arguments in one batch of scalar loads either way).
+struct GroupSel {
+    const uint8_t *Wp;
+    uint16_t *Y;
+    const uint16_t *res;                         // the block glue's residual, or null
+    float scale;
+    int N;
+    int first;                                   // the matrix's first block
+};
+template <bool ONE>
+__device__ __forceinline__ GroupSel select_group(const Groups &gr, const Fusion &fu, int block)
 {
-    int gi = 0;
+    GroupSel s{gr.Wp[0], gr.Y[0], fu.res[0], gr.scale[0], gr.N[0], 0};
+    if constexpr (!ONE) {
 #pragma unroll
-    for (int q = 1; q < kMaxGroups; ++q)
-        if (q < gr.G && block >= gr.blk[q]) gi = q;
-    return gi;
+        for (int q = 1; q < kMaxGroups; ++q)
+            if (q < gr.G && block >= gr.blk[q]) s = GroupSel{gr.Wp[q], gr.Y[q], fu.res[q], gr.scale[q], gr.N[q], gr.blk[q]};
+    }
+    return s;
 }
 
 // Kernel launchers of the layer; arguments are already validated.

@@ -60,17 +60,17 @@ __device__ __forceinline__ float4_t mfma(const u32x4 a, const u32x4 b, float4_t 
 
 }  // namespace
 
-template <int FMT, int NW, int CST, int GL>
+template <int FMT, int NW, int CST, int GL, bool ONE>
 __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X, const Groups gr, int K, int C,
                                                  const Fusion fu)
 {
     constexpr bool NORM = (GL & kGlueNorm) != 0;
     constexpr bool PAIR = (GL & kGluePair) != 0;
-    const int gi = group_of(gr, (int)blockIdx.x);
-    const uint8_t *__restrict__ Wp = gr.Wp[gi];
-    uint16_t *__restrict__ Y = gr.Y[gi];
-    const float scale = gr.scale[gi];
-    const int N = gr.N[gi];
+    const GroupSel grp = select_group<ONE>(gr, fu, (int)blockIdx.x);
+    const uint8_t *__restrict__ Wp = grp.Wp;
+    uint16_t *__restrict__ Y = grp.Y;
+    const float scale = grp.scale;
+    const int N = grp.N;
     constexpr bool TWO = FMT == TRI_FMT_2BIT;
     constexpr int XH = TWO ? 64 : 80;            // activations per chunk
     constexpr int NOP = TWO ? 8 : 10;            // A operands (MFMAs) per chunk
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar descriptors)
     const int g = lane >> 4;
     const int j = lane & 15;
-    const int n0 = ((int)blockIdx.x - gr.blk[gi]) * 16;
+    const int n0 = ((int)blockIdx.x - grp.first) * 16;
     const int64_t S = (int64_t)C * 16;
 
     // (1) activations of this wave's chunks: local chunk l is global chunk
@@ -280,31 +280,32 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
             const float y1 = (sd1 * 16777216.0f - sx) * gr.scale[1] * rinv;
             y = y / (1.f + __expf(-y)) * y1;     // silu(gate) * up
         }
-        if (fu.res[gi]) y += h2f(fu.res[gi][n0 + threadIdx.x]);
+        if (grp.res) y += h2f(grp.res[n0 + threadIdx.x]);
         Y[n0 + threadIdx.x] = __builtin_bit_cast(uint16_t, (_Float16)y);
     }
+}
+
+template <int FMT, int NW, int CST, int GL>
+static void launch_gl(const uint16_t *X, const Groups &gr, int K, int C, hipStream_t s, const Fusion &f)
+{
+    const dim3 grid(gr.blk[gr.G]), block(64 * NW);
+    if (gr.G == 1)
+        hipLaunchKernelGGL((k_mv1<FMT, NW, CST, GL, true>), grid, block, 0, s, X, gr, K, C, f);
+    else
+        hipLaunchKernelGGL((k_mv1<FMT, NW, CST, GL, false>), grid, block, 0, s, X, gr, K, C, f);
 }
 
 template <int FMT, int NW, int CST>
 static void launch_cfg(const uint16_t *X, const Groups &gr, int K, int C, hipStream_t s, const Fusion *fu)
 {
     const Fusion f = fu ? *fu : Fusion{};
-    const dim3 grid(gr.blk[gr.G]), block(64 * NW);
     const int gl = glue_bits(fu);
     if constexpr (NW == 8) {                     // (pair variants: eight waves only, see launch_fmt)
-        if (gl == kGluePair) {
-            hipLaunchKernelGGL((k_mv1<FMT, NW, CST, kGluePair>), grid, block, 0, s, X, gr, K, C, f);
-            return;
-        }
-        if (gl == (kGlueNorm | kGluePair)) {
-            hipLaunchKernelGGL((k_mv1<FMT, NW, CST, kGlueNorm | kGluePair>), grid, block, 0, s, X, gr, K, C, f);
-            return;
-        }
+        if (gl == kGluePair) return launch_gl<FMT, NW, CST, kGluePair>(X, gr, K, C, s, f);
+        if (gl == (kGlueNorm | kGluePair)) return launch_gl<FMT, NW, CST, kGlueNorm | kGluePair>(X, gr, K, C, s, f);
     }
-    if (gl & kGlueNorm)
-        hipLaunchKernelGGL((k_mv1<FMT, NW, CST, kGlueNorm>), grid, block, 0, s, X, gr, K, C, f);
-    else
-        hipLaunchKernelGGL((k_mv1<FMT, NW, CST, 0>), grid, block, 0, s, X, gr, K, C, f);
+    if (gl & kGlueNorm) return launch_gl<FMT, NW, CST, kGlueNorm>(X, gr, K, C, s, f);
+    return launch_gl<FMT, NW, CST, 0>(X, gr, K, C, s, f);
 }
 
 // Eight waves per 16 rows (measured best at K = 4096 and 11008); sixteen for long rows.

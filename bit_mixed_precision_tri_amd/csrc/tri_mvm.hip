@@ -55,23 +55,23 @@ __device__ __forceinline__ void wave_sync()
 
 }  // namespace
 
-template <int FMT, int MT, int NW, int CST, int GL, int RB>
+template <int FMT, int MT, int NW, int CST, int GL, int RB, bool ONE>
 __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X, const Groups gr, int M, int K, int C,
                                                  const Fusion fu)
 {
     constexpr bool NORM = (GL & kGlueNorm) != 0;
     constexpr bool PAIR = (GL & kGluePair) != 0;
     static_assert(!PAIR || RB == 1, "the pair variant owns one 16-row block of each matrix per workgroup");
-    const int gi = group_of(gr, (int)blockIdx.x);
-    const uint8_t *__restrict__ Wp = gr.Wp[gi];
-    const float scale = gr.scale[gi];
-    const int N = gr.N[gi];
+    const GroupSel grp = select_group<ONE>(gr, fu, (int)blockIdx.x);
+    const uint8_t *__restrict__ Wp = grp.Wp;
+    const float scale = grp.scale;
+    const int N = grp.N;
     // more than 16 activation rows: workgroup row y of the grid takes rows 16y .. 16y+15 of X and Y
     const int64_t m_first = 16 * (int64_t)blockIdx.y;
     X += m_first * K;
     M = min(16, M - (int)m_first);
-    uint16_t *__restrict__ Y = gr.Y[gi] + m_first * N;
-    const uint16_t *__restrict__ R = fu.res[gi] ? fu.res[gi] + m_first * N : nullptr;
+    uint16_t *__restrict__ Y = grp.Y + m_first * N;
+    const uint16_t *__restrict__ R = grp.res ? grp.res + m_first * N : nullptr;
     constexpr bool TWO = FMT == TRI_FMT_2BIT;
     constexpr int XH = TWO ? 64 : 80;            // activations per chunk
     constexpr int NOP = TWO ? 8 : 10;            // A operands (MFMAs) per chunk
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar descriptors)
     const int g = lane >> 4;
     const int j = lane & 15;
-    const int n0 = ((int)blockIdx.x - gr.blk[gi]) * 16 * RB;
+    const int n0 = ((int)blockIdx.x - grp.first) * 16 * RB;
     const int64_t S = (int64_t)C * 16;
 
     // activations of step s: piece P = 64i + lane is piece P % RP of row P / RP, i.e. values
@@ -353,8 +353,12 @@ static bool launch_gl(const uint16_t *X, const Groups &gr, int M, int K, int C, 
 {
     if constexpr (has_glue<FMT, MT, NW, CST, GL>() && has_rb<FMT, MT, CST, RB, GL>()) {
         const Groups g = RB == 1 ? gr : regroup(gr, RB);
-        hipLaunchKernelGGL((k_mvm<FMT, MT, NW, CST, GL, RB>), dim3(g.blk[g.G], (M + 15) / 16), dim3(64 * NW), 0, s, X,
-                           g, M, K, C, f);
+        const dim3 grid(g.blk[g.G], (M + 15) / 16), block(64 * NW);
+        // (single-matrix variants for the plain layer only: the glue variants serve grouped launches)
+        if (GL == 0 && g.G == 1)
+            hipLaunchKernelGGL((k_mvm<FMT, MT, NW, CST, GL, RB, GL == 0>), grid, block, 0, s, X, g, M, K, C, f);
+        else
+            hipLaunchKernelGGL((k_mvm<FMT, MT, NW, CST, GL, RB, false>), grid, block, 0, s, X, g, M, K, C, f);
         return true;
     }
     return false;
