@@ -99,9 +99,9 @@ __device__ __forceinline__ GroupSel select_group(const Groups &gr, const Fusion 
 int launch_gemv2(const uint16_t *X, const uint8_t *Wp, float scale, int N, int K, uint16_t *Y, hipStream_t s);
 int launch_smallm(const uint16_t *X, const uint8_t *Wp, float scale, int M, int N, int K, int fmt, uint16_t *Y,
                   hipStream_t s);
-// M = 1 on MFMA (tri_mv1.hip) and 2 <= M <= 16 on MFMA (tri_mvm.hip), for one or several
-// matrices, with the block glue `fu` folded in when it is non-null; false (nothing launched)
-// if the shape is outside their range.
+// M = 1 on MFMA (tri_mv1.hip) and M >= 2 on MFMA (tri_mvm.hip; past 16 rows in 16-row slices,
+// without glue), for one or several matrices, with the block glue `fu` folded in when it is
+// non-null; false (nothing launched) if the shape is outside their range.
 bool launch_mv1(const uint16_t *X, const Groups &gr, int K, int fmt, hipStream_t s, const Fusion *fu = nullptr);
 bool launch_mvm(const uint16_t *X, const Groups &gr, int M, int K, int fmt, hipStream_t s, const Fusion *fu = nullptr);
 // The small-M kernels for one matrix: the two above, else the LDS-staged kernel for short rows;
