@@ -173,7 +173,8 @@ int tri_linear_grouped(const _Float16 *X, const uint8_t *const *Wp, const float 
             y[g] = reinterpret_cast<uint16_t *>(Y[g]);
         }
         const Groups gr = make_groups(G, Wp, scale, n, y);
-        const bool done = M == 1 ? launch_mv1(x, gr, (int)K, fmt, stream) : launch_mvm(x, gr, (int)M, (int)K, fmt, stream);
+        const bool done = M == 1 ? launch_mv1(x, gr, (int)K, fmt, stream)
+                          : (M == 2 && launch_mv2(x, gr, (int)K, fmt, stream)) || launch_mvm(x, gr, (int)M, (int)K, fmt, stream);
         if (done) return hipGetLastError() == hipSuccess ? TRI_OK : TRI_EHIP;
     }
     // shapes outside the grouped kernels' range: one call per matrix
@@ -222,7 +223,8 @@ int tri_linear_fused(const _Float16 *X, const uint8_t *const *Wp, const float *s
     if (pair) gr.blk[2] = gr.blk[1];            // the grid covers matrix 0's rows; each workgroup reads both
     const uint16_t *x = reinterpret_cast<const uint16_t *>(X);
     const bool done =
-        M == 1 ? launch_mv1(x, gr, (int)K, fmt, stream, &fu) : launch_mvm(x, gr, (int)M, (int)K, fmt, stream, &fu);
+        M == 1 ? launch_mv1(x, gr, (int)K, fmt, stream, &fu)
+               : (M == 2 && launch_mv2(x, gr, (int)K, fmt, stream, &fu)) || launch_mvm(x, gr, (int)M, (int)K, fmt, stream, &fu);
     if (!done) return TRI_EINVAL;                // a shape the glue variants do not serve
     return hipGetLastError() == hipSuccess ? TRI_OK : TRI_EHIP;
 }

@@ -60,10 +60,11 @@ __device__ __forceinline__ float4_t mfma(const u32x4 a, const u32x4 b, float4_t 
 
 }  // namespace
 
-template <int FMT, int NW, int CST, int GL, bool ONE>
-__global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X, const Groups gr, int K, int C,
+template <int FMT, int NW, int CST, int GL, bool ONE, int MR>
+__global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X, const Groups gr, int M, int K, int C,
                                                  const Fusion fu)
 {
+    static_assert(MR == 1 || (MR == 2 && GL == 0), "two activation rows: the plain layer (and the residual) only");
     constexpr bool NORM = (GL & kGlueNorm) != 0;
     constexpr bool PAIR = (GL & kGluePair) != 0;
     const GroupSel grp = select_group<ONE>(gr, fu, (int)blockIdx.x);
@@ -79,9 +80,9 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
     constexpr int PIECES = XH / 8;               // 16-byte activation pieces per chunk
     constexpr int NLD = (NCH * PIECES + 63) / 64;   // whole-line activation loads per lane
     static_assert(NCH <= 64, "chunks per wave");
-    __shared__ u32x4 xa[NW][NCH][NOP];           // per wave: A operands of its chunks
+    __shared__ u32x4 xa[NW][NCH][MR][NOP];       // per wave: A operands of its chunks, per activation row
     __shared__ u32x4 xraw[TWO ? 1 : NW][TWO ? 1 : NCH * PIECES];   // 1.6-bit: raw pieces
-    __shared__ float red[NW][NORM ? 18 : 17];    // per wave: the 16 rows, sum x (, sum x^2)
+    __shared__ float red[NW][MR][NORM ? 18 : 17];   // per wave and activation row: the 16 outputs, sum x (, sum x^2)
     __shared__ float red1[PAIR ? NW : 1][16];    // pair: the second matrix's rows
 
     const int lane = threadIdx.x & 63;
@@ -94,20 +95,24 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
     // (1) activations of this wave's chunks: local chunk l is global chunk
     //     4*((l/4)*NW + w) + l%4; piece P = 64i + lane of the wave's pieces is piece P % PIECES
     //     of local chunk P / PIECES, so a load instruction reads whole 128-byte lines
-    const __amdgpu_buffer_rsrc_t xr = rsrc(X, (uint32_t)K * 2u);
-    u32x4 xv[NLD], nv[NORM ? NLD : 1];
+    //     (several activation rows: the same pieces of each row, rows past M reading as zero)
+    const __amdgpu_buffer_rsrc_t xr =
+        rsrc(X, __builtin_amdgcn_readfirstlane((uint32_t)min(M, MR) * (uint32_t)K * 2u));
+    u32x4 xv[MR][NLD], nv[NORM ? NLD : 1];
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-        const int P = 64 * i + lane;
-        const int l = P / PIECES;
-        const int gc = 4 * ((l >> 2) * NW + wv) + (l & 3);
-        const int k = gc * XH + 8 * (P % PIECES);
-        const int off = (l < NCH && k < K) ? (int)((uint32_t)k * 2u) : (int)0x80000000u;
-        xv[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
-        if constexpr (NORM) {                    // the norm gain of the same activations
-            if (fu.gain) nv[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc(fu.gain, (uint32_t)K * 2u), off, 0, 0);
+    for (int r = 0; r < MR; ++r)
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            const int P = 64 * i + lane;
+            const int l = P / PIECES;
+            const int gc = 4 * ((l >> 2) * NW + wv) + (l & 3);
+            const int k = gc * XH + 8 * (P % PIECES);
+            const int off = (l < NCH && k < K) ? (int)((uint32_t)(r * K + k) * 2u) : (int)0x80000000u;
+            xv[r][i] = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
+            if constexpr (NORM) {                // the norm gain of the same activations
+                if (fu.gain) nv[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc(fu.gain, (uint32_t)K * 2u), off, 0, 0);
+            }
         }
-    }
     // (2) every weight chunk of the wave, all in flight at once
     const int rows_here = min(16, N - n0);
     const __amdgpu_buffer_rsrc_t wr =
@@ -132,64 +137,80 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
         for (int i = 0; i < NLD; ++i)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                xsq = dot2(xv[i][e], xv[i][e], xsq);
-                if (fu.gain) xv[i][e] = mul2(xv[i][e], nv[i][e]);
+                xsq = dot2(xv[0][i][e], xv[0][i][e], xsq);
+                if (fu.gain) xv[0][i][e] = mul2(xv[0][i][e], nv[i][e]);
             }
     }
-    float xsum = 0.f;
+    float xsum[MR];
 #pragma unroll
-    for (int i = 0; i < NLD; ++i)
+    for (int r = 0; r < MR; ++r) {
+        xsum[r] = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) xsum = dot2(xv[i][e], 0x3C003C00u, xsum);   // (x_lo, x_hi) . (1, 1)
+        for (int i = 0; i < NLD; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) xsum[r] = dot2(xv[r][i][e], 0x3C003C00u, xsum[r]);   // (x_lo, x_hi) . (1, 1)
+    }
     if constexpr (TWO) {
         // lanes 2v, 2v+1 of a chunk's eight hold x[16v .. 16v+7] and x[16v+8 .. 16v+15]: they swap
         // pieces (DPP quad_perm [1,0,3,2]); the even lane forms positions 0..3, the odd one 4..7
         const bool odd = lane & 1;
         const int vv = (lane & 7) >> 1;
 #pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-            const int l = (64 * i + lane) / PIECES;
-            u32x4 other;
+        for (int r = 0; r < MR; ++r)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) other[e] = (uint32_t)__builtin_amdgcn_mov_dpp((int)xv[i][e], 0xB1, 0xF, 0xF, false);
-            const u32x4 lo = odd ? other : xv[i];
-            const u32x4 hi = odd ? xv[i] : other;
+            for (int i = 0; i < NLD; ++i) {
+                const int l = (64 * i + lane) / PIECES;
+                u32x4 other;
 #pragma unroll
-            for (int pp = 0; pp < 4; ++pp) {
-                const uint32_t dlo = odd ? lo[2 + pp / 2] : lo[pp / 2];
-                const uint32_t dhi = odd ? hi[2 + pp / 2] : hi[pp / 2];
-                const uint32_t r = (pp & 1) ? pair_halves<1>(dhi, dlo) : pair_halves<0>(dhi, dlo);
-                if (l < NCH) reinterpret_cast<uint32_t *>(&xa[wv][l][pp + (odd ? 4 : 0)])[vv] = r;
-            }
-        }
-    } else {
-        // the pairing of a 40-value half spans ten pieces: bounce the raw pieces through LDS
+                for (int e = 0; e < 4; ++e)
+                    other[e] = (uint32_t)__builtin_amdgcn_mov_dpp((int)xv[r][i][e], 0xB1, 0xF, 0xF, false);
+                const u32x4 lo = odd ? other : xv[r][i];
+                const u32x4 hi = odd ? xv[r][i] : other;
 #pragma unroll
-        for (int i = 0; i < NLD; ++i)
-            if (64 * i + lane < NCH * PIECES) xraw[wv][64 * i + lane] = xv[i];
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (lane < NCH) {
-            uint32_t x32[40];
-#pragma unroll
-            for (int q = 0; q < 10; ++q) {
-                const u32x4 v = xraw[wv][10 * lane + q];
-                x32[4 * q] = v[0]; x32[4 * q + 1] = v[1]; x32[4 * q + 2] = v[2]; x32[4 * q + 3] = v[3];
-            }
-#pragma unroll
-            for (int p = 0; p < 5; ++p)
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    u32x4 a;
-#pragma unroll
-                    for (int qq = 0; qq < 4; ++qq) {
-                        const int e = 5 * (4 * hh + qq) + p;   // value index; partner e + 40
-                        a[qq] = (e & 1) ? pair_halves<1>(x32[(e >> 1) + 20], x32[e >> 1])
-                                        : pair_halves<0>(x32[(e >> 1) + 20], x32[e >> 1]);
-                    }
-                    xa[wv][lane][2 * p + hh] = a;
+                for (int pp = 0; pp < 4; ++pp) {
+                    const uint32_t dlo = odd ? lo[2 + pp / 2] : lo[pp / 2];
+                    const uint32_t dhi = odd ? hi[2 + pp / 2] : hi[pp / 2];
+                    const uint32_t v = (pp & 1) ? pair_halves<1>(dhi, dlo) : pair_halves<0>(dhi, dlo);
+                    if (l < NCH) reinterpret_cast<uint32_t *>(&xa[wv][l][r][pp + (odd ? 4 : 0)])[vv] = v;
                 }
+            }
+    } else {
+        // the pairing of a 40-value half spans ten pieces: bounce the raw pieces through LDS,
+        // one activation row at a time
+#pragma unroll
+        for (int r = 0; r < MR; ++r) {
+            if (r > 0) {                         // the previous row's pieces have been read
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            }
+#pragma unroll
+            for (int i = 0; i < NLD; ++i)
+                if (64 * i + lane < NCH * PIECES) xraw[wv][64 * i + lane] = xv[r][i];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if (lane < NCH) {
+                uint32_t x32[40];
+#pragma unroll
+                for (int q = 0; q < 10; ++q) {
+                    const u32x4 v = xraw[wv][10 * lane + q];
+                    x32[4 * q] = v[0]; x32[4 * q + 1] = v[1]; x32[4 * q + 2] = v[2]; x32[4 * q + 3] = v[3];
+                }
+#pragma unroll
+                for (int p = 0; p < 5; ++p)
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        u32x4 av;
+#pragma unroll
+                        for (int qq = 0; qq < 4; ++qq) {
+                            const int e = 5 * (4 * hh + qq) + p;   // value index; partner e + 40
+                            av[qq] = (e & 1) ? pair_halves<1>(x32[(e >> 1) + 20], x32[e >> 1])
+                                             : pair_halves<0>(x32[(e >> 1) + 20], x32[e >> 1]);
+                        }
+                        xa[wv][lane][r][2 * p + hh] = av;
+                    }
+            }
         }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -226,7 +247,7 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
 #pragma unroll
     for (int s = 0; s < CST; ++s) {
         if (4 * (s * NW + wv) >= C) break;       // wave-uniform: no chunk of this step is live
-        const u32x4 *asrc = &xa[wv][4 * s + g][0];
+        const u32x4 *asrc = &xa[wv][4 * s + g][j % MR][0];   // A row j: activation row j % MR
         u32x4 a[NOP];
 #pragma unroll
         for (int p = 0; p < NOP; ++p) a[p] = asrc[p];
@@ -234,8 +255,9 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
         if constexpr (PAIR) contract(a, wq1[s], acc1);
     }
 
-    // (5) merge classes (every row of a D tile is the same; row 0 is element 0 of lanes 0..15),
-    //     add the waves' partial sums in a fixed order, subtract sum_k x, scale, round
+    // (5) merge classes (D row i holds activation row i % MR; rows 0..MR-1 are elements 0..MR-1
+    //     of lanes 0..15), add the waves' partial sums in a fixed order, subtract sum_k x, scale,
+    //     round
     auto merge = [&](const float4_t (&ac)[NCLS]) __attribute__((always_inline)) {
         if constexpr (!TWO) return ac[0] + ac[1];
         float4_t t = ac[0] + 0.25f * ac[1];
@@ -243,11 +265,13 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
         t += 0.00390625f * ac[4] + 0.0009765625f * ac[5];
         return t;
     };
-    float xw[1] = {xsum};
-    const float xs_wave = wave_reduce_rows<1>(xw, lane);
+    const float xs_wave = wave_reduce_rows<MR>(xsum, lane);   // lane group r (of 64 / MR lanes): row r
     const float4_t t = merge(acc);
-    if (g == 0) red[wv][j] = t[0];
-    if (lane == 0) red[wv][16] = xs_wave;
+    if (g == 0) {
+#pragma unroll
+        for (int e = 0; e < MR; ++e) red[wv][e][j] = t[e];
+    }
+    if ((lane & (64 / MR - 1)) == 0) red[wv][lane / (64 / MR)][16] = xs_wave;
     if constexpr (PAIR) {
         const float4_t t1 = merge(acc1);
         if (g == 0) red1[wv][j] = t1[0];
@@ -255,62 +279,77 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
     if constexpr (NORM) {
         float xq[1] = {xsq};
         const float xq_wave = wave_reduce_rows<1>(xq, lane);
-        if (lane == 0) red[wv][17] = xq_wave;
+        if (lane == 0) red[wv][0][17] = xq_wave;
     }
     __syncthreads();
-    if (threadIdx.x < 16 && n0 + (int)threadIdx.x < N) {
+    const int e = threadIdx.x >> 4, jj = threadIdx.x & 15;   // thread (e, jj): output Y[e][n0 + jj]
+    if (threadIdx.x < 16 * MR && e < M && n0 + jj < N) {
         float sd = 0.f, sx = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
-            sd += red[w][threadIdx.x];
-            sx += red[w][16];
+            sd += red[w][e][jj];
+            sx += red[w][e][16];
         }
         float rinv = 1.f;
         if constexpr (NORM) {
             float sq = 0.f;
 #pragma unroll
-            for (int w = 0; w < NW; ++w) sq += red[w][17];
+            for (int w = 0; w < NW; ++w) sq += red[w][0][17];
             rinv = 1.f / sqrtf(sq / (float)K + fu.eps);
         }
         float y = (sd * 16777216.0f - sx) * scale * rinv;
         if constexpr (PAIR) {
             float sd1 = 0.f;
 #pragma unroll
-            for (int w = 0; w < NW; ++w) sd1 += red1[w][threadIdx.x];
+            for (int w = 0; w < NW; ++w) sd1 += red1[w][jj];
             const float y1 = (sd1 * 16777216.0f - sx) * gr.scale[1] * rinv;
             y = y / (1.f + __expf(-y)) * y1;     // silu(gate) * up
         }
-        if (grp.res) y += h2f(grp.res[n0 + threadIdx.x]);
-        Y[n0 + threadIdx.x] = __builtin_bit_cast(uint16_t, (_Float16)y);
+        const int64_t o = (int64_t)e * N + n0 + jj;
+        if (grp.res) y += h2f(grp.res[o]);
+        Y[o] = __builtin_bit_cast(uint16_t, (_Float16)y);
     }
 }
 
-template <int FMT, int NW, int CST, int GL>
-static void launch_gl(const uint16_t *X, const Groups &gr, int K, int C, hipStream_t s, const Fusion &f)
+template <int FMT, int NW, int CST, int GL, int MR>
+static bool launch_gl(const uint16_t *X, const Groups &gr, int M, int K, int C, hipStream_t s, const Fusion &f)
 {
-    const dim3 grid(gr.blk[gr.G]), block(64 * NW);
-    if (gr.G == 1)
-        hipLaunchKernelGGL((k_mv1<FMT, NW, CST, GL, true>), grid, block, 0, s, X, gr, K, C, f);
-    else
-        hipLaunchKernelGGL((k_mv1<FMT, NW, CST, GL, false>), grid, block, 0, s, X, gr, K, C, f);
+    // several activation rows: only while the staged A operands of the workgroup stay below
+    // 100 KB of LDS
+    constexpr int kXaBytes = NW * 4 * CST * MR * (FMT == TRI_FMT_2BIT ? 8 : 10) * 16;
+    if constexpr (MR > 1 && kXaBytes > 100 * 1024) {
+        return false;
+    } else {
+        const dim3 grid(gr.blk[gr.G]), block(64 * NW);
+        if (gr.G == 1)
+            hipLaunchKernelGGL((k_mv1<FMT, NW, CST, GL, true, MR>), grid, block, 0, s, X, gr, M, K, C, f);
+        else
+            hipLaunchKernelGGL((k_mv1<FMT, NW, CST, GL, false, MR>), grid, block, 0, s, X, gr, M, K, C, f);
+        return true;
+    }
 }
 
-template <int FMT, int NW, int CST>
-static void launch_cfg(const uint16_t *X, const Groups &gr, int K, int C, hipStream_t s, const Fusion *fu)
+template <int FMT, int NW, int CST, int MR>
+static bool launch_cfg(const uint16_t *X, const Groups &gr, int M, int K, int C, hipStream_t s, const Fusion *fu)
 {
     const Fusion f = fu ? *fu : Fusion{};
-    const int gl = glue_bits(fu);
-    if constexpr (NW == 8) {                     // (pair variants: eight waves only, see launch_fmt)
-        if (gl == kGluePair) return launch_gl<FMT, NW, CST, kGluePair>(X, gr, K, C, s, f);
-        if (gl == (kGlueNorm | kGluePair)) return launch_gl<FMT, NW, CST, kGlueNorm | kGluePair>(X, gr, K, C, s, f);
+    if constexpr (MR > 1) {
+        return launch_gl<FMT, NW, CST, 0, MR>(X, gr, M, K, C, s, f);   // (no glue but the residual)
+    } else {
+        const int gl = glue_bits(fu);
+        if constexpr (NW == 8) {                 // (pair variants: eight waves only, see launch_fmt)
+            if (gl == kGluePair) return launch_gl<FMT, NW, CST, kGluePair, 1>(X, gr, M, K, C, s, f);
+            if (gl == (kGlueNorm | kGluePair))
+                return launch_gl<FMT, NW, CST, kGlueNorm | kGluePair, 1>(X, gr, M, K, C, s, f);
+        }
+        if (gl & kGlueNorm) return launch_gl<FMT, NW, CST, kGlueNorm, 1>(X, gr, M, K, C, s, f);
+        return launch_gl<FMT, NW, CST, 0, 1>(X, gr, M, K, C, s, f);
     }
-    if (gl & kGlueNorm) return launch_gl<FMT, NW, CST, kGlueNorm>(X, gr, K, C, s, f);
-    return launch_gl<FMT, NW, CST, 0>(X, gr, K, C, s, f);
 }
 
 // Eight waves per 16 rows (measured best at K = 4096 and 11008 for 2-bit); sixteen for long rows.
-template <int FMT>
-static bool launch_fmt(const uint16_t *X, const Groups &gr, int K, int C, hipStream_t s, const Fusion *fu)
+template <int FMT, int MR>
+static bool launch_fmt(const uint16_t *X, const Groups &gr, int M, int K, int C, hipStream_t s, const Fusion *fu)
 {
     // 1.6-bit rows of up to 64 chunks: four waves with twice the steps each, so a wave's decode
     // of one step overlaps the arrival of the next (3-6% faster at K = 4096; equal at 11008, and
@@ -318,33 +357,36 @@ static bool launch_fmt(const uint16_t *X, const Groups &gr, int K, int C, hipStr
     if constexpr (FMT == TRI_FMT_1P6BIT) {
         if (!glue_bits(fu) && C <= 64) {
             switch ((C + 15) / 16) {
-            case 1: launch_cfg<FMT, 4, 1>(X, gr, K, C, s, fu); return true;
-            case 2: launch_cfg<FMT, 4, 2>(X, gr, K, C, s, fu); return true;
-            case 3: launch_cfg<FMT, 4, 3>(X, gr, K, C, s, fu); return true;
-            default: launch_cfg<FMT, 4, 4>(X, gr, K, C, s, fu); return true;
+            case 1: return launch_cfg<FMT, 4, 1, MR>(X, gr, M, K, C, s, fu);
+            case 2: return launch_cfg<FMT, 4, 2, MR>(X, gr, M, K, C, s, fu);
+            case 3: return launch_cfg<FMT, 4, 3, MR>(X, gr, M, K, C, s, fu);
+            default: return launch_cfg<FMT, 4, 4, MR>(X, gr, M, K, C, s, fu);
             }
         }
     }
     const int cst8 = (C + 31) / 32;              // chunk-steps with 8 waves (4 chunks per step and wave)
     switch (cst8) {
-    case 1: launch_cfg<FMT, 8, 1>(X, gr, K, C, s, fu); return true;
-    case 2: launch_cfg<FMT, 8, 2>(X, gr, K, C, s, fu); return true;
-    case 3: launch_cfg<FMT, 8, 3>(X, gr, K, C, s, fu); return true;
-    case 4: launch_cfg<FMT, 8, 4>(X, gr, K, C, s, fu); return true;
-    case 5: launch_cfg<FMT, 8, 5>(X, gr, K, C, s, fu); return true;
-    case 6: launch_cfg<FMT, 8, 6>(X, gr, K, C, s, fu); return true;
-    case 7: launch_cfg<FMT, 8, 7>(X, gr, K, C, s, fu); return true;
-    case 8: launch_cfg<FMT, 8, 8>(X, gr, K, C, s, fu); return true;
+    case 1: return launch_cfg<FMT, 8, 1, MR>(X, gr, M, K, C, s, fu);
+    case 2: return launch_cfg<FMT, 8, 2, MR>(X, gr, M, K, C, s, fu);
+    case 3: return launch_cfg<FMT, 8, 3, MR>(X, gr, M, K, C, s, fu);
+    case 4: return launch_cfg<FMT, 8, 4, MR>(X, gr, M, K, C, s, fu);
+    case 5: return launch_cfg<FMT, 8, 5, MR>(X, gr, M, K, C, s, fu);
+    case 6: return launch_cfg<FMT, 8, 6, MR>(X, gr, M, K, C, s, fu);
+    case 7: return launch_cfg<FMT, 8, 7, MR>(X, gr, M, K, C, s, fu);
+    case 8: return launch_cfg<FMT, 8, 8, MR>(X, gr, M, K, C, s, fu);
     default: break;
     }
-    // sixteen waves; the staged activations of a workgroup must fit in LDS.  (The pair variant
-    // would exceed the registers a wave has at sixteen waves: longer rows are not paired.)
-    if (fu && fu->pair) return false;
-    const int cst16 = (C + 63) / 64;
-    if (cst16 <= 6) { launch_cfg<FMT, 16, 6>(X, gr, K, C, s, fu); return true; }
-    if constexpr (FMT == TRI_FMT_2BIT) {
-        if (cst16 <= 8) { launch_cfg<FMT, 16, 8>(X, gr, K, C, s, fu); return true; }
-        if (cst16 <= 12) { launch_cfg<FMT, 16, 12>(X, gr, K, C, s, fu); return true; }
+    // sixteen waves (one activation row); the staged activations of a workgroup must fit in LDS.
+    // (The pair variant would exceed the registers a wave has at sixteen waves: longer rows are
+    // not paired.)
+    if constexpr (MR == 1) {
+        if (fu && fu->pair) return false;
+        const int cst16 = (C + 63) / 64;
+        if (cst16 <= 6) return launch_cfg<FMT, 16, 6, 1>(X, gr, M, K, C, s, fu);
+        if constexpr (FMT == TRI_FMT_2BIT) {
+            if (cst16 <= 8) return launch_cfg<FMT, 16, 8, 1>(X, gr, M, K, C, s, fu);
+            if (cst16 <= 12) return launch_cfg<FMT, 16, 12, 1>(X, gr, M, K, C, s, fu);
+        }
     }
     return false;                                // longer rows: the streaming small-M kernel
 }
@@ -356,8 +398,19 @@ bool launch_mv1(const uint16_t *X, const Groups &gr, int K, int fmt, hipStream_t
     // activations are read in pieces of 8 values, so K must be a multiple of 8
     if ((K % 8) != 0 || (int64_t)K * 2 >= ((int64_t)1 << 31) || 16 * (int64_t)C * 16 >= ((int64_t)1 << 31))
         return false;
-    return fmt == TRI_FMT_2BIT ? launch_fmt<TRI_FMT_2BIT>(X, gr, K, C, s, fu)
-                             : launch_fmt<TRI_FMT_1P6BIT>(X, gr, K, C, s, fu);
+    return fmt == TRI_FMT_2BIT ? launch_fmt<TRI_FMT_2BIT, 1>(X, gr, 1, K, C, s, fu)
+                             : launch_fmt<TRI_FMT_1P6BIT, 1>(X, gr, 1, K, C, s, fu);
+}
+
+bool launch_mv2(const uint16_t *X, const Groups &gr, int K, int fmt, hipStream_t s, const Fusion *fu)
+{
+    const int C = (int)(row_bytes(K, fmt) / 16);
+    // (as above, for the two activation rows; of the glue, the residual only)
+    if (glue_bits(fu) || (K % 8) != 0 || (int64_t)2 * K * 2 >= ((int64_t)1 << 31) ||
+        16 * (int64_t)C * 16 >= ((int64_t)1 << 31))
+        return false;
+    return fmt == TRI_FMT_2BIT ? launch_fmt<TRI_FMT_2BIT, 2>(X, gr, 2, K, C, s, fu)
+                             : launch_fmt<TRI_FMT_1P6BIT, 2>(X, gr, 2, K, C, s, fu);
 }
 
 }  // namespace tri

@@ -91,7 +91,7 @@ PAIRED = [
     dict(name="pair+norm+gain", pair=True, norm=True, gain=True),
     dict(name="pair+norm+residual", pair=True, norm=True, res=True),
 ]
-SHAPES = [(1, 4096), (3, 1000), (8, 11008), (16, 4096), (1, 11008), (12, 1000)]
+SHAPES = [(1, 4096), (2, 4096), (3, 1000), (8, 11008), (16, 4096), (1, 11008), (12, 1000)]
 
 
 def inputs(M, K, Ns, seed):
@@ -165,7 +165,7 @@ def test_fused_norm_multi_block_workgroups(fmt, M):
 @pytest.mark.parametrize("fmt", FMTS)
 def test_fused_without_glue_equals_grouped_bitwise(fmt):
     import torch
-    for (M, K) in [(1, 4096), (5, 1000), (16, 11008)]:
+    for (M, K) in [(1, 4096), (2, 4096), (5, 1000), (16, 11008)]:
         Ns = [64, 300]
         Ws, scales, X, _, _ = inputs(M, K, Ns, 981)
         Wps = [tri.pack(cuda(W), fmt) for W in Ws]

@@ -94,7 +94,9 @@ RAGGED = [(1, 1, 1), (1, 37, 1000), (1, 130, 4097), (1, 300, 81), (1, 33, 12000)
           # a middling M: the GEMM on quarter-width tiles (at most 64 tiles) and on half-width ones
           (100, 11000, 1000), (300, 16001, 72),
           # long rows: 9..16 steps per wave of eight (2-bit and 1.6-bit), and past that the streaming kernel
-          (5, 300, 24000), (16, 200, 30000), (8, 100, 40000), (12, 100, 40000), (20, 90, 26000)]
+          (5, 300, 24000), (16, 200, 30000), (8, 100, 40000), (12, 100, 40000), (20, 90, 26000),
+          # two activation rows on the M = 1 kernel's structure (eight and four waves, up to 8 steps)
+          (2, 300, 1000), (2, 4100, 4096), (2, 1000, 11008), (2, 90, 16384), (2, 50, 20000)]
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -350,7 +352,7 @@ def test_gemm_full_tiles_ragged_edges(fmt):
 # Grouped layers: several matrices reading the same activations, one launch where the small-M
 # kernels serve every matrix (K = 1000: the grouped kernels, also over 16-row slices for M > 16;
 # K = 1001: one launch per matrix).
-GROUPED = [(1, 1000), (3, 1000), (16, 1000), (1, 1001), (5, 1001), (20, 1000), (40, 1000), (20, 1001)]
+GROUPED = [(1, 1000), (2, 1000), (3, 1000), (16, 1000), (1, 1001), (5, 1001), (20, 1000), (40, 1000), (20, 1001)]
 
 
 @pytest.mark.parametrize("fmt", FMTS)
