@@ -178,6 +178,38 @@ def cpu_baseline(shapes, budget_s=10.0):
                       "median %.3f s per step" % (len(times), budget_s, t)}
 
 
+def cpu_oracle_detail(shapes):
+    """The oracle beside the GPU in more detail (bounded, a few seconds): the decode step on one
+    thread, and the prefill layer (8192 -> 28672, 2-bit) on a fixed 16-row subset of its 2048
+    rows on every thread, extrapolated to all rows."""
+    import numpy as np
+    import oracle
+    from bit_mixed_precision_tri_amd import configs, synth
+    threads = oracle.max_threads()              # (before the one-thread runs, which set the OpenMP count)
+    work = []
+    for li, (name, K, N) in enumerate(shapes):
+        W, X, s = synth.layer_inputs(configs.DECODE["workload_id"], li, 1, N, K)
+        work.append((X, oracle.pack2(W), K, s))
+    one = []
+    for _ in range(2):
+        t0 = time.perf_counter()
+        for (X, Wp, K, s) in work:
+            oracle.linear_packed_f64(X, Wp, K, 0, s, nthreads=1)
+        one.append(time.perf_counter() - t0)
+    pc = configs.PREFILL
+    name, K, N = pc["shapes"][0]
+    W = synth.trits(synth.rng_for(pc["workload_id"], 0, synth.STREAM_W), N, K)
+    X = synth.activations(synth.rng_for(pc["workload_id"], 0, synth.STREAM_X), 16, K)
+    Wp = oracle.pack2(W)
+    del W
+    t0 = time.perf_counter()
+    oracle.linear_packed_f64(X, Wp, K, 0, pc["scale"], nthreads=threads)
+    tp = (time.perf_counter() - t0) * pc["M"] / 16
+    return {"decode_step_1_thread_s": round(float(np.median(one)), 4),
+            "prefill_%s_2bit" % name: {"rows_timed": 16, "threads": threads, "extrapolated_s": round(tp, 2),
+                                        "TFLOPs": round(2 * pc["M"] * N * K / tp / 1e12, 5)}}
+
+
 def capture(layers, steps):
     """A HIP graph of `steps` decode steps (each: every layer once, next weight copy)."""
     import torch
@@ -305,6 +337,7 @@ def main():
         out["quantize"] = bench_quantize(clock)
     if not args.skip_cpu:
         out["cpu_baseline"] = cpu_baseline(dcfg["shapes"])
+        out["cpu_oracle_detail"] = cpu_oracle_detail(dcfg["shapes"])
     print(json.dumps(out), flush=True)
 
 
