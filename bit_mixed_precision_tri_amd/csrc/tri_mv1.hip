@@ -1,4 +1,5 @@
-// tri_mv1.hip -- ternary linear layer for one activation row (M = 1, decode) on MFMA.
+// tri_mv1.hip -- ternary linear layer for one activation row (M = 1, decode) on MFMA, and for
+// two rows with the same structure.
 //
 // The layer (Pith review of "Spectra 1.1", "What carries the argument"):
 //   y[n] = scale * sum_k t[n][k] * x[k],  t in {-1, 0, +1},  fp32 accumulation.
@@ -30,7 +31,9 @@
 // chunks past a row's end meet zero activations).  The wave loads the activations of its own
 // chunks with whole-line loads, permutes them into the A-operand order in LDS (no
 // workgroup barrier), and adds them up for sum_k x.  The waves' partial sums meet in LDS and
-// are added in a fixed order (no atomics).
+// are added in a fixed order (no atomics).  With two activation rows (MR = 2) both rows are
+// staged the same way and A row i holds activation row i % 2, so D rows 0 and 1 are the two
+// outputs.
 //
 // Block glue.  Every variant adds an optional residual to the fp32 result before rounding.
 // Norm variant (GL & kGlueNorm): the norm gain is read beside the activations; each lane adds

@@ -1,4 +1,4 @@
-// tri_mvm.hip -- ternary linear layer for a few activation rows (2 <= M <= 16, batched decode)
+// tri_mvm.hip -- ternary linear layer for a few activation rows (batched decode, up to 16 rows)
 // on MFMA; more rows run as 16-row slices in one launch (a second grid dimension), the weights
 // of a row block then being read once per slice.
 //
@@ -11,9 +11,9 @@
 // from multiply-shift quotients, d * 2^-24, one accumulator per half chunk), and
 // sum_k X[m][k] subtracted once per output at the end.
 //
-// Work split.  A workgroup of NW waves owns 16 weight rows; wave w takes chunk-steps s, where
-// lane (g = lane/16, j = lane%16) reads 16-byte chunk c = 4*(s*NW + w) + g of weight row j and
-// supplies the activations of row j of X (as A operand) for the same chunk.  All weight chunks
+// Work split.  A workgroup of NW waves owns RB blocks of 16 weight rows; wave w takes chunk-steps
+// s, where lane (g = lane/16, j = lane%16) reads 16-byte chunk c = 4*(s*NW + w) + g of row j of
+// every block and supplies the activations of row j of X (as A operand) for the same chunk.  All weight chunks
 // of the wave are requested at the start.  The activations of a step -- four consecutive
 // chunks of every activation row -- are read with whole-line loads one step ahead, bounced
 // through the wave's LDS slot to the lanes that use them, and permuted there into the
