@@ -63,11 +63,12 @@ __device__ __forceinline__ float4_t mfma(const u32x4 a, const u32x4 b, float4_t 
 
 }  // namespace
 
-template <int FMT, int NW, int CST, int GL, bool ONE, int MR>
+template <int FMT, int NW, int CST, int GL, bool ONE, int MR, int RB>
 __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X, const Groups gr, int M, int K, int C,
                                                  const Fusion fu)
 {
     static_assert(MR == 1 || (MR == 2 && GL == 0), "two activation rows: the plain layer (and the residual) only");
+    static_assert(RB == 1 || GL == 0, "several row blocks: the plain layer (and the residual) only");
     constexpr bool NORM = (GL & kGlueNorm) != 0;
     constexpr bool PAIR = (GL & kGluePair) != 0;
     const GroupSel grp = select_group<ONE>(gr, fu, (int)blockIdx.x);
@@ -85,14 +86,15 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
     static_assert(NCH <= 64, "chunks per wave");
     __shared__ u32x4 xa[NW][NCH][MR][NOP];       // per wave: A operands of its chunks, per activation row
     __shared__ u32x4 xraw[TWO ? 1 : NW][TWO ? 1 : NCH * PIECES];   // 1.6-bit: raw pieces
-    __shared__ float red[NW][MR][NORM ? 18 : 17];   // per wave and activation row: the 16 outputs, sum x (, sum x^2)
+    // per wave and activation row: the 16 outputs of each block, sum x (, sum x^2)
+    __shared__ float red[NW][MR][16 * RB + (NORM ? 2 : 1)];
     __shared__ float red1[PAIR ? NW : 1][16];    // pair: the second matrix's rows
 
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar descriptors)
     const int g = lane >> 4;
     const int j = lane & 15;
-    const int n0 = ((int)blockIdx.x - grp.first) * 16;
+    const int n0 = ((int)blockIdx.x - grp.first) * 16 * RB;
     const int64_t S = (int64_t)C * 16;
 
     // (1) activations of this wave's chunks: local chunk l is global chunk
@@ -117,18 +119,21 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
             }
         }
     // (2) every weight chunk of the wave, all in flight at once
-    const int rows_here = min(16, N - n0);
+    const int rows_here = min(16 * RB, N - n0);
     const __amdgpu_buffer_rsrc_t wr =
         rsrc(Wp + (int64_t)n0 * S, __builtin_amdgcn_readfirstlane((uint32_t)(rows_here * S)));
     // (pair: the same chunks of the second matrix, requested in the order they are used)
     const __amdgpu_buffer_rsrc_t wr1 =
         rsrc(gr.Wp[PAIR ? 1 : 0] + (int64_t)n0 * S, __builtin_amdgcn_readfirstlane((uint32_t)(rows_here * S)));
-    u32x4 wq[CST], wq1[PAIR ? CST : 1];
+    u32x4 wq[RB][CST], wq1[PAIR ? CST : 1];
 #pragma unroll
     for (int s = 0; s < CST; ++s) {
         const int c = 4 * (s * NW + wv) + g;
         const int off = c < C ? (int)(uint32_t)(j * S + c * 16) : (int)0x80000000u;
-        wq[s] = __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 0);
+#pragma unroll
+        for (int r = 0; r < RB; ++r)             // (rows past the matrix's end read as zero)
+            wq[r][s] = __builtin_amdgcn_raw_buffer_load_b128(
+                wr, c < C ? (int)(uint32_t)((16 * r + j) * S + c * 16) : (int)0x80000000u, 0, 0);
         if constexpr (PAIR) wq1[s] = __builtin_amdgcn_raw_buffer_load_b128(wr1, off, 0, 0);
     }
 
@@ -222,9 +227,11 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
 
     // (4) decode and contract, one MFMA per position (and half, 1.6-bit)
     const float4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-    float4_t acc[NCLS], acc1[PAIR ? NCLS : 1];
+    float4_t acc[RB][NCLS], acc1[PAIR ? NCLS : 1];
 #pragma unroll
-    for (int c = 0; c < NCLS; ++c) acc[c] = zero4;
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int c = 0; c < NCLS; ++c) acc[r][c] = zero4;
 #pragma unroll
     for (int c = 0; c < (PAIR ? NCLS : 1); ++c) acc1[c] = zero4;
     auto contract = [&](const u32x4 (&a)[NOP], const u32x4 v, float4_t (&ac)[NCLS]) __attribute__((always_inline)) {
@@ -254,7 +261,8 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
         u32x4 a[NOP];
 #pragma unroll
         for (int p = 0; p < NOP; ++p) a[p] = asrc[p];
-        contract(a, wq[s], acc);
+#pragma unroll
+        for (int r = 0; r < RB; ++r) contract(a, wq[r][s], acc[r]);
         if constexpr (PAIR) contract(a, wq1[s], acc1);
     }
 
@@ -269,12 +277,15 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
         return t;
     };
     const float xs_wave = wave_reduce_rows<MR>(xsum, lane);   // lane group r (of 64 / MR lanes): row r
-    const float4_t t = merge(acc);
-    if (g == 0) {
 #pragma unroll
-        for (int e = 0; e < MR; ++e) red[wv][e][j] = t[e];
+    for (int r = 0; r < RB; ++r) {
+        const float4_t t = merge(acc[r]);
+        if (g == 0) {
+#pragma unroll
+            for (int e = 0; e < MR; ++e) red[wv][e][16 * r + j] = t[e];
+        }
     }
-    if ((lane & (64 / MR - 1)) == 0) red[wv][lane / (64 / MR)][16] = xs_wave;
+    if ((lane & (64 / MR - 1)) == 0) red[wv][lane / (64 / MR)][16 * RB] = xs_wave;
     if constexpr (PAIR) {
         const float4_t t1 = merge(acc1);
         if (g == 0) red1[wv][j] = t1[0];
@@ -282,22 +293,22 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
     if constexpr (NORM) {
         float xq[1] = {xsq};
         const float xq_wave = wave_reduce_rows<1>(xq, lane);
-        if (lane == 0) red[wv][0][17] = xq_wave;
+        if (lane == 0) red[wv][0][16 * RB + 1] = xq_wave;
     }
     __syncthreads();
-    const int e = threadIdx.x >> 4, jj = threadIdx.x & 15;   // thread (e, jj): output Y[e][n0 + jj]
-    if (threadIdx.x < 16 * MR && e < M && n0 + jj < N) {
+    const int e = threadIdx.x / (16 * RB), jj = threadIdx.x % (16 * RB);   // thread (e, jj): output Y[e][n0 + jj]
+    if (threadIdx.x < 16 * RB * MR && e < M && n0 + jj < N) {
         float sd = 0.f, sx = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
             sd += red[w][e][jj];
-            sx += red[w][e][16];
+            sx += red[w][e][16 * RB];
         }
         float rinv = 1.f;
         if constexpr (NORM) {
             float sq = 0.f;
 #pragma unroll
-            for (int w = 0; w < NW; ++w) sq += red[w][0][17];
+            for (int w = 0; w < NW; ++w) sq += red[w][0][16 * RB + 1];
             rinv = 1.f / sqrtf(sq / (float)K + fu.eps);
         }
         float y = (sd * 16777216.0f - sx) * scale * rinv;
@@ -314,7 +325,7 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
     }
 }
 
-template <int FMT, int NW, int CST, int GL, int MR>
+template <int FMT, int NW, int CST, int GL, int MR, int RB>
 static bool launch_gl(const uint16_t *X, const Groups &gr, int M, int K, int C, hipStream_t s, const Fusion &f)
 {
     // several activation rows: only while the staged A operands of the workgroup stay below
@@ -323,30 +334,54 @@ static bool launch_gl(const uint16_t *X, const Groups &gr, int M, int K, int C, 
     if constexpr (MR > 1 && kXaBytes > 100 * 1024) {
         return false;
     } else {
-        const dim3 grid(gr.blk[gr.G]), block(64 * NW);
-        if (gr.G == 1)
-            hipLaunchKernelGGL((k_mv1<FMT, NW, CST, GL, true, MR>), grid, block, 0, s, X, gr, M, K, C, f);
+        const Groups g = RB == 1 ? gr : regroup(gr, RB);
+        const dim3 grid(g.blk[g.G]), block(64 * NW);
+        if (g.G == 1)
+            hipLaunchKernelGGL((k_mv1<FMT, NW, CST, GL, true, MR, RB>), grid, block, 0, s, X, g, M, K, C, f);
         else
-            hipLaunchKernelGGL((k_mv1<FMT, NW, CST, GL, false, MR>), grid, block, 0, s, X, gr, M, K, C, f);
+            hipLaunchKernelGGL((k_mv1<FMT, NW, CST, GL, false, MR, RB>), grid, block, 0, s, X, g, M, K, C, f);
         return true;
     }
+}
+
+// Four 16-row blocks per workgroup (2-bit, eight waves, no glue but the residual): every
+// activation value a wave stages feeds four blocks.  It pays only on wide matrices -- 4096 ->
+// 14336: 6.21 -> 5.86 us at M = 1, 6.78 -> 5.92 us at M = 2 -- and loses where fewer than about
+// 200 such workgroups remain (4096 -> 11008: 5.03 -> 5.24 us; two blocks lose everywhere measured
+// but there), so it is taken from 200 workgroups on.
+template <int FMT, int NW, int CST, int MR>
+static bool wide_rb(const Groups &gr, const Fusion *fu)
+{
+    if constexpr (FMT != TRI_FMT_2BIT || NW != 8 || (MR == 2 && CST > 6)) return false;
+    else return !glue_bits(fu) && regroup(gr, 4).blk[gr.G] >= 200;
 }
 
 template <int FMT, int NW, int CST, int MR>
 static bool launch_cfg(const uint16_t *X, const Groups &gr, int M, int K, int C, hipStream_t s, const Fusion *fu)
 {
     const Fusion f = fu ? *fu : Fusion{};
-    if constexpr (MR > 1) {
-        return launch_gl<FMT, NW, CST, 0, MR>(X, gr, M, K, C, s, f);   // (no glue but the residual)
+    const bool rb4 = wide_rb<FMT, NW, CST, MR>(gr, fu);
+    if constexpr (MR > 1) {                      // (no glue but the residual)
+        if constexpr (FMT == TRI_FMT_2BIT && NW == 8 && CST <= 6) {
+            if (rb4) return launch_gl<FMT, NW, CST, 0, MR, 4>(X, gr, M, K, C, s, f);
+        }
+        return launch_gl<FMT, NW, CST, 0, MR, 1>(X, gr, M, K, C, s, f);
     } else {
         const int gl = glue_bits(fu);
         if constexpr (NW == 8) {                 // (pair variants: eight waves only, see launch_fmt)
-            if (gl == kGluePair) return launch_gl<FMT, NW, CST, kGluePair, 1>(X, gr, M, K, C, s, f);
+            if (gl == kGluePair) return launch_gl<FMT, NW, CST, kGluePair, 1, 1>(X, gr, M, K, C, s, f);
             if (gl == (kGlueNorm | kGluePair))
-                return launch_gl<FMT, NW, CST, kGlueNorm | kGluePair, 1>(X, gr, M, K, C, s, f);
+                return launch_gl<FMT, NW, CST, kGlueNorm | kGluePair, 1, 1>(X, gr, M, K, C, s, f);
         }
-        if (gl & kGlueNorm) return launch_gl<FMT, NW, CST, kGlueNorm, 1>(X, gr, M, K, C, s, f);
-        return launch_gl<FMT, NW, CST, 0, 1>(X, gr, M, K, C, s, f);
+        if constexpr (NW == 16) {                // (the norm serves rows of up to eight steps: eight waves)
+            if (gl) return false;
+        } else {
+            if (gl & kGlueNorm) return launch_gl<FMT, NW, CST, kGlueNorm, 1, 1>(X, gr, M, K, C, s, f);
+        }
+        if constexpr (FMT == TRI_FMT_2BIT && NW == 8) {
+            if (rb4) return launch_gl<FMT, NW, CST, 0, 1, 4>(X, gr, M, K, C, s, f);
+        }
+        return launch_gl<FMT, NW, CST, 0, 1, 1>(X, gr, M, K, C, s, f);
     }
 }
 

@@ -328,27 +328,6 @@ constexpr bool has_rb()
     return false;
 }
 
-// The grid of RB-block workgroups: matrix g owns workgroups blk[g] .. blk[g+1]-1.
-Groups regroup(const Groups &gr, int RB)
-{
-    Groups g = gr;
-    for (int q = 0; q < gr.G; ++q) g.blk[q + 1] = g.blk[q] + (gr.N[q] + 16 * RB - 1) / (16 * RB);
-    for (int q = gr.G; q < kMaxGroups; ++q) g.blk[q + 1] = g.blk[gr.G];
-    return g;
-}
-
-// Blocks per workgroup: the largest RB whose grid (over every 16-row slice of the activations)
-// still gives 5/8 of a workgroup per CU.  Fewer, fuller workgroups win down to about that
-// point (measured at M = 4..64 on 4096 -> 11008, 11008 -> 4096 and 4096 -> 4096: 172
-// four-block workgroups beat 688 one-block ones by 15-25%; 128 lose to 256).
-int choose_rb(const Groups &gr, int M)
-{
-    const int64_t slices = (M + 15) / 16;
-    for (int rb = 4; rb > 1; rb /= 2)
-        if (regroup(gr, rb).blk[gr.G] * slices >= kCUs * 5 / 8) return rb;
-    return 1;
-}
-
 template <int FMT, int MT, int NW, int CST, int GL, int RB>
 static bool launch_gl(const uint16_t *X, const Groups &gr, int M, int K, int C, hipStream_t s, const Fusion &f)
 {

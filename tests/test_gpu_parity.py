@@ -96,7 +96,9 @@ RAGGED = [(1, 1, 1), (1, 37, 1000), (1, 130, 4097), (1, 300, 81), (1, 33, 12000)
           # long rows: 9..16 steps per wave of eight (2-bit and 1.6-bit), and past that the streaming kernel
           (5, 300, 24000), (16, 200, 30000), (8, 100, 40000), (12, 100, 40000), (20, 90, 26000),
           # two activation rows on the M = 1 kernel's structure (eight and four waves, up to 8 steps)
-          (2, 300, 1000), (2, 4100, 4096), (2, 1000, 11008), (2, 90, 16384), (2, 50, 20000)]
+          (2, 300, 1000), (2, 4100, 4096), (2, 1000, 11008), (2, 90, 16384), (2, 50, 20000),
+          # wide matrices: the decode kernel with four 16-row blocks per workgroup (2-bit)
+          (1, 13000, 1000), (2, 12900, 2048), (1, 14336, 4096)]
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -377,13 +379,14 @@ def test_grouped_layers(fmt, case):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("M", [8, 16, 24])
+@pytest.mark.parametrize("M", [1, 2, 8, 16, 24])
 def test_grouped_large_grid_same_as_single(fmt, M):
-    """Q, K, V-like projections (3 x 4096 rows): the grouped grid is large enough for workgroups of
-    several 16-row blocks while each single layer's is not; the results are bitwise the same."""
+    """Q, K, V-like projections (3 x 4096 rows; 3 x 8192 at M <= 2): the grouped grid is large
+    enough for workgroups of several 16-row blocks while each single layer's is not; the results
+    are bitwise the same."""
     import torch
     K = 1000
-    Ns = [4096, 4096, 4096]
+    Ns = [8192, 8192, 8192] if M <= 2 else [4096, 4096, 4096]
     X = synth.activations(synth.rng_for(410 + fmt, M, synth.STREAM_X), M, K)
     Ws = [synth.trits(synth.rng_for(410 + fmt, 10 * M + g, synth.STREAM_W), n, K) for g, n in enumerate(Ns)]
     scales = [0.02, -0.03, 0.045]
