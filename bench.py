@@ -292,11 +292,11 @@ def main():
         shapes_out.append({"shape": name, "K": K, "N": N, "bytes": L.bytes, "kernel_us": round(t * 1e6, 3),
                            "GBps": round(L.bytes / t / 1e9, 1),
                            "algo": tri.ALGO_NAMES[tri.tri_select_algo(1, N, K, F2)]})
-    # the small-M MFMA kernels at M = 1, same shapes (kernel choice evidence)
+    # the VALU GEMV kernel at M = 1, same shapes (the alternative the MFMA kernel is chosen over)
     for so, L in zip(shapes_out, layers):
-        t, _ = clock.run([lambda L=L: L.launch(tri.TRI_ALGO_SMALLM)] * 100)
-        so["smallm_kernel_us"] = round(t * 1e6, 3)
-        so["smallm_GBps"] = round(L.bytes / t / 1e9, 1)
+        t, _ = clock.run([lambda L=L: L.launch(tri.TRI_ALGO_GEMV)] * 100)
+        so["gemv_kernel_us"] = round(t * 1e6, 3)
+        so["gemv_GBps"] = round(L.bytes / t / 1e9, 1)
     del layers
     torch.cuda.empty_cache()
     floors = []
@@ -304,6 +304,8 @@ def main():
         nb = N * tri.tri_row_bytes(K, F2)
         t = read_floor(nb, clock)
         floors.append({"shape": name, "bytes": nb, "read_us": round(t * 1e6, 3), "GBps": round(nb / t / 1e9, 1)})
+    for so, fl in zip(shapes_out, floors):      # the read floor's time over the kernel's: 1.0 = at the floor
+        so["read_floor_over_kernel"] = round(fl["read_us"] / so["kernel_us"], 3)
     ctr = counters()
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
