@@ -174,7 +174,8 @@ int tri_linear_grouped(const _Float16 *X, const uint8_t *const *Wp, const float 
         }
         const Groups gr = make_groups(G, Wp, scale, n, y);
         const bool done = M == 1 ? launch_mv1(x, gr, (int)K, fmt, stream)
-                          : (M == 2 && launch_mv2(x, gr, (int)K, fmt, stream)) || launch_mvm(x, gr, (int)M, (int)K, fmt, stream);
+                          : (M <= 4 && launch_mvr(x, gr, (int)M, (int)K, fmt, stream)) ||
+                                launch_mvm(x, gr, (int)M, (int)K, fmt, stream);
         if (done) return hipGetLastError() == hipSuccess ? TRI_OK : TRI_EHIP;
     }
     // shapes outside the grouped kernels' range: one call per matrix
@@ -224,7 +225,8 @@ int tri_linear_fused(const _Float16 *X, const uint8_t *const *Wp, const float *s
     const uint16_t *x = reinterpret_cast<const uint16_t *>(X);
     const bool done =
         M == 1 ? launch_mv1(x, gr, (int)K, fmt, stream, &fu)
-               : (M == 2 && launch_mv2(x, gr, (int)K, fmt, stream, &fu)) || launch_mvm(x, gr, (int)M, (int)K, fmt, stream, &fu);
+               : (M <= 4 && launch_mvr(x, gr, (int)M, (int)K, fmt, stream, &fu)) ||
+                     launch_mvm(x, gr, (int)M, (int)K, fmt, stream, &fu);
     if (!done) return TRI_EINVAL;                // a shape the glue variants do not serve
     return hipGetLastError() == hipSuccess ? TRI_OK : TRI_EHIP;
 }

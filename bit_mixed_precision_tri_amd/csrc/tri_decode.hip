@@ -260,7 +260,7 @@ bool launch_decode(const uint16_t *X, const uint8_t *Wp, float scale, int M, int
         return false;
     const Groups gr = make_groups(1, &Wp, &scale, &N, &Y);
     if (M == 1) return launch_mv1(X, gr, K, fmt, s);
-    if (M == 2 && launch_mv2(X, gr, K, fmt, s)) return true;
+    if (M <= 4 && launch_mvr(X, gr, M, K, fmt, s)) return true;
     if (launch_mvm(X, gr, M, K, fmt, s)) return true;
     return fmt == TRI_FMT_2BIT ? launch_mn<TRI_FMT_2BIT>(X, Wp, scale, M, N, K, C, Y, s)
                                : launch_mn<TRI_FMT_1P6BIT>(X, Wp, scale, M, N, K, C, Y, s);

@@ -124,9 +124,10 @@ int launch_smallm(const uint16_t *X, const uint8_t *Wp, float scale, int M, int 
 // without glue), for one or several matrices, with the block glue `fu` folded in when it is
 // non-null; false (nothing launched) if the shape is outside their range.
 bool launch_mv1(const uint16_t *X, const Groups &gr, int K, int fmt, hipStream_t s, const Fusion *fu = nullptr);
-// M = 2 on the M = 1 kernel's structure (of the glue, the residual only): all of a wave's
-// activations of both rows are staged at once, and A row i of the MFMA holds activation row i % 2.
-bool launch_mv2(const uint16_t *X, const Groups &gr, int K, int fmt, hipStream_t s, const Fusion *fu = nullptr);
+// M = 2 (both formats) and M = 3, 4 (2-bit) on the M = 1 kernel's structure (of the glue, the
+// residual only): all of a wave's activations of every row are staged at once, and A row i of
+// the MFMA holds activation row i % MR (MR = 2 or 4).
+bool launch_mvr(const uint16_t *X, const Groups &gr, int M, int K, int fmt, hipStream_t s, const Fusion *fu = nullptr);
 bool launch_mvm(const uint16_t *X, const Groups &gr, int M, int K, int fmt, hipStream_t s, const Fusion *fu = nullptr);
 // The small-M kernels for one matrix: the two above, else the LDS-staged kernel for short rows;
 // false (nothing launched) if none of them takes the shape.

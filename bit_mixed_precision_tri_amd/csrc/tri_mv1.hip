@@ -67,7 +67,7 @@ template <int FMT, int NW, int CST, int GL, bool ONE, int MR, int RB>
 __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X, const Groups gr, int M, int K, int C,
                                                  const Fusion fu)
 {
-    static_assert(MR == 1 || (MR == 2 && GL == 0), "two activation rows: the plain layer (and the residual) only");
+    static_assert(MR == 1 || ((MR == 2 || MR == 4) && GL == 0), "several activation rows: the plain layer (and the residual) only");
     static_assert(RB == 1 || GL == 0, "several row blocks: the plain layer (and the residual) only");
     constexpr bool NORM = (GL & kGlueNorm) != 0;
     constexpr bool PAIR = (GL & kGluePair) != 0;
@@ -345,15 +345,23 @@ static bool launch_gl(const uint16_t *X, const Groups &gr, int M, int K, int C, 
 }
 
 // Four 16-row blocks per workgroup (2-bit, eight waves, no glue but the residual): every
-// activation value a wave stages feeds four blocks.  It pays only on wide matrices -- 4096 ->
-// 14336: 6.21 -> 5.86 us at M = 1, 6.78 -> 5.92 us at M = 2 -- and loses where fewer than about
-// 200 such workgroups remain (4096 -> 11008: 5.03 -> 5.24 us; two blocks lose everywhere measured
-// but there), so it is taken from 200 workgroups on.
+// activation value a wave stages feeds four blocks.  At one or two rows it pays only while the
+// grid of four-block workgroups fills most CUs once (4096 -> 14336, 224 of them: 5.48 -> 5.25 us
+// at M = 1) and loses both below about 200 (4096 -> 11008: 5.03 -> 5.24 us) and past one per CU,
+// where the last ones run alone (2 x 11008 grouped, 344: 7.01 -> 8.50 us).  At four rows the
+// activation traffic weighs more and it wins from about 160 on (4096 -> 11008 at M = 4: 6.98 ->
+// 5.89 us).  Two blocks lost wherever four did not win, so they are not used.
 template <int FMT, int NW, int CST, int MR>
 static bool wide_rb(const Groups &gr, const Fusion *fu)
 {
-    if constexpr (FMT != TRI_FMT_2BIT || NW != 8 || (MR == 2 && CST > 6)) return false;
-    else return !glue_bits(fu) && regroup(gr, 4).blk[gr.G] >= 200;
+    if constexpr (FMT != TRI_FMT_2BIT || NW != 8 || (MR == 2 && CST > 6)) {
+        return false;
+    } else {
+        const int w = regroup(gr, 4).blk[gr.G];
+        if (glue_bits(fu)) return false;
+        if constexpr (MR == 4) return w >= 160;
+        else return w >= (MR == 1 ? 200 : 160) && w <= kCUs;
+    }
 }
 
 template <int FMT, int NW, int CST, int MR>
@@ -362,7 +370,7 @@ static bool launch_cfg(const uint16_t *X, const Groups &gr, int M, int K, int C,
     const Fusion f = fu ? *fu : Fusion{};
     const bool rb4 = wide_rb<FMT, NW, CST, MR>(gr, fu);
     if constexpr (MR > 1) {                      // (no glue but the residual)
-        if constexpr (FMT == TRI_FMT_2BIT && NW == 8 && CST <= 6) {
+        if constexpr (FMT == TRI_FMT_2BIT && NW == 8 && (MR == 4 || CST <= 6)) {
             if (rb4) return launch_gl<FMT, NW, CST, 0, MR, 4>(X, gr, M, K, C, s, f);
         }
         return launch_gl<FMT, NW, CST, 0, MR, 1>(X, gr, M, K, C, s, f);
@@ -440,15 +448,18 @@ bool launch_mv1(const uint16_t *X, const Groups &gr, int K, int fmt, hipStream_t
                              : launch_fmt<TRI_FMT_1P6BIT, 1>(X, gr, 1, K, C, s, fu);
 }
 
-bool launch_mv2(const uint16_t *X, const Groups &gr, int K, int fmt, hipStream_t s, const Fusion *fu)
+bool launch_mvr(const uint16_t *X, const Groups &gr, int M, int K, int fmt, hipStream_t s, const Fusion *fu)
 {
     const int C = (int)(row_bytes(K, fmt) / 16);
-    // (as above, for the two activation rows; of the glue, the residual only)
-    if (glue_bits(fu) || (K % 8) != 0 || (int64_t)2 * K * 2 >= ((int64_t)1 << 31) ||
+    // (as above, for up to four activation rows; of the glue, the residual only)
+    if (M < 2 || M > 4 || glue_bits(fu) || (K % 8) != 0 || (int64_t)4 * K * 2 >= ((int64_t)1 << 31) ||
         16 * (int64_t)C * 16 >= ((int64_t)1 << 31))
         return false;
-    return fmt == TRI_FMT_2BIT ? launch_fmt<TRI_FMT_2BIT, 2>(X, gr, 2, K, C, s, fu)
-                             : launch_fmt<TRI_FMT_1P6BIT, 2>(X, gr, 2, K, C, s, fu);
+    if (fmt == TRI_FMT_2BIT)
+        return M == 2 ? launch_fmt<TRI_FMT_2BIT, 2>(X, gr, M, K, C, s, fu)
+                      : launch_fmt<TRI_FMT_2BIT, 4>(X, gr, M, K, C, s, fu);
+    // 1.6-bit: two rows only (four measured 10-50% slower than the batched kernel)
+    return M == 2 && launch_fmt<TRI_FMT_1P6BIT, 2>(X, gr, M, K, C, s, fu);
 }
 
 }  // namespace tri

@@ -98,7 +98,9 @@ RAGGED = [(1, 1, 1), (1, 37, 1000), (1, 130, 4097), (1, 300, 81), (1, 33, 12000)
           # two activation rows on the M = 1 kernel's structure (eight and four waves, up to 8 steps)
           (2, 300, 1000), (2, 4100, 4096), (2, 1000, 11008), (2, 90, 16384), (2, 50, 20000),
           # wide matrices: the decode kernel with four 16-row blocks per workgroup (2-bit)
-          (1, 13000, 1000), (2, 12900, 2048), (1, 14336, 4096)]
+          (1, 13000, 1000), (2, 12900, 2048), (1, 14336, 4096),
+          # three and four rows on the same structure (2-bit; 1.6-bit takes the batched kernel)
+          (3, 300, 1000), (4, 11000, 4096), (4, 4100, 11008), (3, 10300, 2000), (4, 50, 16384)]
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -379,7 +381,7 @@ def test_grouped_layers(fmt, case):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("M", [1, 2, 8, 16, 24])
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 16, 24])
 def test_grouped_large_grid_same_as_single(fmt, M):
     """Q, K, V-like projections (3 x 4096 rows; 3 x 8192 at M <= 2): the grouped grid is large
     enough for workgroups of several 16-row blocks while each single layer's is not; the results
