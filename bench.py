@@ -236,7 +236,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--skip-extra", action="store_true", help="skip the batched, block and prefill workloads")
     ap.add_argument("--skip-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--profile", choices=["decode", "copy"],
+    ap.add_argument("--profile", choices=["decode", "copy", "prefill"],
                     help="only launch one workload a few times (for rocprofv3 --pmc runs)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -588,6 +588,16 @@ def profile_mode(which):
         for _ in range(20):
             for L in layers:
                 L.launch()
+    elif which == "prefill":
+        cfg = configs.PREFILL
+        name, K, N = cfg["shapes"][0]
+        for fmt in cfg["fmts"]:
+            L = Layer(cfg["workload_id"], 0, cfg["M"], N, K, fmt, scale=cfg["scale"], copies=1)
+            for _ in range(3):
+                L.launch()
+            torch.cuda.synchronize()
+            del L
+            torch.cuda.empty_cache()
     elif which == "copy":
         nb = 64 << 20
         src = torch.ones(nb, dtype=torch.uint8, device="cuda")
