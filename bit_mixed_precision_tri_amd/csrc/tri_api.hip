@@ -28,29 +28,32 @@ int check_linear(const void *X, const void *Wp, int64_t M, int64_t N, int64_t K,
 
 // The kernel family for a shape.  Up to 16 rows, the small-M kernels (at M = 1 the MFMA kernel
 // beats the VALU GEMV).  Above, the small-M kernels take one pass over the weights per 16-row
-// slice of X, while the GEMM's parallelism comes from its 128 x 512 output tiles alone, so with
-// few tiles most CUs idle.  Both costs per unit of K, from fits to measured times on MI355X
-// (M = 17 .. 512; K x N = 4096 x 4096, 4096 x 11008, 11008 x 4096, 8192 x 28672, 28672 x 8192;
-// both formats):
-//   small-M  ceil(M/16) * N * c,  c = 0.10 ps (2-bit) / 0.15 ps (1.6-bit) per trit and slice;
+// slice of X, while the GEMM's parallelism comes from its output tiles alone, so with few tiles
+// most CUs idle.  Both costs per unit of K, from fits to measured times on MI355X (M = 17 .. 768;
+// K x N = 4096 x 4096, 4096 x 11008, 11008 x 4096, 8192 x 28672, 28672 x 8192; both formats):
+//   small-M  ceil(M/16) * N * c,  c = 0.10 ps (2-bit) / 0.127 ps (1.6-bit) per trit and slice;
 //            rows past eight steps per wave 1.6x / 1.2x that, rows past sixteen (the streaming
 //            kernel) 5x / 1.9x;
-//   GEMM     T = ceil(M/128) * ceil(N/512) tiles; at most 64: one round of quarter-width
-//            tiles, 8 ns (2-bit) / 9 ns (1.6-bit); else u * R, u = 11 ns / 13.3 ns per round
-//            of half-width tiles, R = the rounds of its launch (a last round of at most 128
-//            tiles runs at half width).
+//   GEMM     with T64 = ceil(M/64) * ceil(N/512) tiles of 64 rows: at most 64 of them, one round
+//            of 64 x 128 workgroups, 4.8 ns (2-bit) / 6.3 ns (1.6-bit); at most 128, 8.8 / 10.7
+//            ns; beyond, u * R with u = 13 / 16 ns per round of 128 x 256 workgroups and R the
+//            rounds of the launch of 128-row tiles (a last round of at most 128 tiles runs at half
+//            width).
 int select_algo(int64_t M, int64_t N, int64_t K, int fmt)
 {
     if (M <= 16) return TRI_ALGO_SMALLM;
     const bool two = fmt == TRI_FMT_2BIT;
-    double c = two ? 0.10 : 0.15;                // ps
+    double c = two ? 0.10 : 0.127;               // ps
     if (K > (two ? 32768 : 35840)) c *= two ? 5.0 : 1.9;
     else if (K > (two ? 16384 : 20480)) c *= two ? 1.6 : 1.2;
-    const int64_t T = ((M + 127) / 128) * ((N + 511) / 512);
+    const int64_t tn = (N + 511) / 512;
+    const int64_t T64 = ((M + 63) / 64) * tn, T = ((M + 127) / 128) * tn;
     const int64_t r = T % kCUs;
     const int64_t R = (r > 0 && r <= kCUs / 2) ? 2 * (T / kCUs) + 1 : 2 * ((T + kCUs - 1) / kCUs);
     const double small = (double)((M + 15) / 16) * (double)N * c;
-    const double gemm = T <= kCUs / 4 ? (two ? 8000.0 : 9000.0) : (two ? 11000.0 : 13300.0) * (double)R;
+    const double gemm = T64 <= kCUs / 4 ? (two ? 4800.0 : 6300.0)
+                      : T64 <= kCUs / 2 ? (two ? 8800.0 : 10700.0)
+                                        : (two ? 13000.0 : 16000.0) * (double)R;
     return small < gemm ? TRI_ALGO_SMALLM : TRI_ALGO_GEMM;
 }
 

@@ -77,15 +77,18 @@ constexpr int kBM = 128;             // rows of Y per workgroup
 constexpr int kMT = 4;               // 32-row MFMA tiles per wave
 constexpr int kBN = 512;             // columns of Y per tile (4 waves side by side, 4 MFMA tiles each)
 
-// A workgroup computes one 128 x 512 tile of Y (NT = 4), one half of it, 128 x 256 (NT = 2), or
-// one quarter, 128 x 128 (NT = 1): part blockIdx.x % (4/NT) of tile tile_base + blockIdx.x / (4/NT)
-// in the tile order.
-template <int FMT, int NT>
+// A workgroup computes one BM x 512 tile of Y (NT = 4), one half of it, BM x 256 (NT = 2), or one
+// quarter, BM x 128 (NT = 1): part blockIdx.x % (4/NT) of tile tile_base + blockIdx.x / (4/NT) in
+// the tile order.  BM is 128, or 64 for a middling M (each wave then covers 64 rows).
+template <int FMT, int NT, int BM>
 __global__ __launch_bounds__(256) void k_gemm(const uint16_t *__restrict__ X, const uint8_t *__restrict__ Wp,
                                               float scale, int M, int N, int K, int C, int tiles_m, int tiles_n,
                                               int tile_base, uint16_t *__restrict__ Y)
 {
     constexpr int kNT = NT;                      // 32-column MFMA tiles per wave
+    constexpr int kBMt = BM;                     // rows of Y per workgroup (128, or 64 for few rows)
+    constexpr int kMTt = BM / 32;                // 32-row MFMA tiles per wave
+    static_assert(BM == 128 || BM == 64, "tile heights");
     constexpr bool TWO = FMT == TRI_FMT_2BIT;
     constexpr int BK = TWO ? 128 : 160;          // trits per K tile (32 packed bytes per weight row)
     constexpr int KS = BK / 16;                  // MFMA k-steps per K tile
@@ -95,9 +98,9 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t *__restrict__ X, co
     constexpr int GV = TWO ? 16 : 40;            // values per group
     constexpr int GPR = BK / GV;                 // groups per row and K tile (8 or 4)
     constexpr int GP = GV / 8;                   // 16-byte pieces per group
-    constexpr int NG = kBM * GPR / 256;          // groups per thread and K tile
+    constexpr int NG = kBMt * GPR / 256;          // groups per thread and K tile
     constexpr int XP = NG * GP;                  // 16-byte pieces per thread and K tile
-    __shared__ uint16_t abuf[2][kBM * ASTR];
+    __shared__ uint16_t abuf[2][kBMt * ASTR];
     __shared__ uint32_t lut[TWO ? 1 : 256];
 
     const int tid = threadIdx.x;
@@ -123,14 +126,14 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t *__restrict__ X, co
     const int in_band = t - band * kGM * tiles_n;
     const int tm = first_m + in_band % band_m;
     const int tn = in_band / band_m;
-    const int m0 = tm * kBM;
+    const int m0 = tm * kBMt;
     const int n0 = tn * kBN + (bid % kParts) * (kBN / kParts) + 32 * kNT * wv;   // this wave's first column
 
     if constexpr (!TWO) {
         lut[tid] = base3_digits_2bit((uint32_t)tid);   // 256 threads, one entry each
     }
 
-    const uint32_t xbytes = __builtin_amdgcn_readfirstlane((uint32_t)((int64_t)min(kBM, M - m0) * K * 2));
+    const uint32_t xbytes = __builtin_amdgcn_readfirstlane((uint32_t)((int64_t)min(kBMt, M - m0) * K * 2));
     const __amdgpu_buffer_rsrc_t xr = rsrc(X + (int64_t)m0 * K, xbytes);
     // weights: lane (h, c) of column tile nt reads row n0 + 32nt + c, bytes 16h.. of each slice
     const int64_t S = (int64_t)C * 16;
@@ -208,9 +211,9 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t *__restrict__ X, co
         }
     };
 
-    float16_t acc[kMT][kNT];
+    float16_t acc[kMTt][kNT];
 #pragma unroll
-    for (int mt = 0; mt < kMT; ++mt)
+    for (int mt = 0; mt < kMTt; ++mt)
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) acc[mt][nt] = float16_t{};
     uint32_t bias;
@@ -260,9 +263,9 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t *__restrict__ X, co
     __syncthreads();                             // tile 0's activations and the byte table
     take_codes(w0);
     const int aoff = c * ASTR + 8 * h;
-    u32x4 afr[kMT], bop[kNT];
+    u32x4 afr[kMTt], bop[kNT];
 #pragma unroll
-    for (int mt = 0; mt < kMT; ++mt) afr[mt] = *reinterpret_cast<const u32x4 *>(&abuf[0][aoff + 32 * mt * ASTR]);
+    for (int mt = 0; mt < kMTt; ++mt) afr[mt] = *reinterpret_cast<const u32x4 *>(&abuf[0][aoff + 32 * mt * ASTR]);
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) bop[nt] = decode(w0, 0, nt);
 
@@ -278,28 +281,28 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t *__restrict__ X, co
             // every wave has stored its share of the next tile (step KS - 2) and read its
             // last operands of this one: the next tile's buffer may be read from here on
             if (MORE && s == KS - 1) __syncthreads();
-            u32x4 an[kMT], bn[kNT];
+            u32x4 an[kMTt], bn[kNT];
             if (s + 1 < KS) {
 #pragma unroll
-                for (int mt = 0; mt < kMT; ++mt)
+                for (int mt = 0; mt < kMTt; ++mt)
                     an[mt] = *reinterpret_cast<const u32x4 *>(acur + 32 * mt * ASTR + 16 * (s + 1));
 #pragma unroll
                 for (int nt = 0; nt < kNT; ++nt) bn[nt] = decode(wc, s + 1, nt);
             } else if (MORE) {
 #pragma unroll
-                for (int mt = 0; mt < kMT; ++mt) an[mt] = *reinterpret_cast<const u32x4 *>(anext + 32 * mt * ASTR);
+                for (int mt = 0; mt < kMTt; ++mt) an[mt] = *reinterpret_cast<const u32x4 *>(anext + 32 * mt * ASTR);
                 take_codes(wx);                  // the last decode of this tile's codes was at step KS - 2
 #pragma unroll
                 for (int nt = 0; nt < kNT; ++nt) bn[nt] = decode(wx, 0, nt);
             }
 #pragma unroll
-            for (int mt = 0; mt < kMT; ++mt)
+            for (int mt = 0; mt < kMTt; ++mt)
 #pragma unroll
                 for (int nt = 0; nt < kNT; ++nt) acc[mt][nt] = mfma32(afr[mt], bop[nt], acc[mt][nt]);
             if (MORE && s == KS - 2) store_a(buf ^ 1, xa);
             // interleave: each MFMA is followed by a share of the next step's decode and reads
 #pragma unroll
-            for (int i = 0; i < kMT * kNT; ++i) {
+            for (int i = 0; i < kMTt * kNT; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
                 __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // 3 VALU
                 if (i % 4 == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
@@ -309,7 +312,7 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t *__restrict__ X, co
             if (MORE && s == KS - 1) load_b(kt + 2, wc);   // wc's last decode was at step KS - 2
             if (s + 1 < KS || MORE) {
 #pragma unroll
-                for (int mt = 0; mt < kMT; ++mt) afr[mt] = an[mt];
+                for (int mt = 0; mt < kMTt; ++mt) afr[mt] = an[mt];
 #pragma unroll
                 for (int nt = 0; nt < kNT; ++nt) bop[nt] = bn[nt];
             }
@@ -327,7 +330,7 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t *__restrict__ X, co
 
     // epilogue: lane (h, c) holds rows 32mt + 8i + 4h + v of column 32nt + c
 #pragma unroll
-    for (int mt = 0; mt < kMT; ++mt)
+    for (int mt = 0; mt < kMTt; ++mt)
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) {
             const int n = n0 + 32 * nt + c;
@@ -350,12 +353,15 @@ static int launch_fmt(const uint16_t *X, const uint8_t *Wp, float scale, int M, 
     const int tiles_n = (N + kBN - 1) / kBN;
     const int64_t T = (int64_t)tiles_m * tiles_n;
     if (T >= ((int64_t)1 << 30)) return TRI_EINVAL;
-    // Few tiles (a middling M): quarter-width tiles, four workgroups per tile, so four times as
-    // many CUs take part (1.4x faster at 64 tiles and below; above, where two quarter-width
-    // workgroups would share a CU, 10-15% slower than half-width ones, measured)
-    if (T <= kCUs / 4) {
-        hipLaunchKernelGGL((k_gemm<FMT, 1>), dim3((unsigned)(4 * T)), dim3(256), 0, s, X, Wp, scale, M, N, K, C, tiles_m,
-                           tiles_n, 0, Y);
+    // Few tiles even of 64 rows (a middling M): 64 x 128 workgroups, four per 64 x 512 tile -- no
+    // half-empty 128-row tiles, and twice the workgroups of 128-row quarter tiles (30-40% faster
+    // where there are at most 64 such tiles; up to 128, two workgroups share a CU and still win
+    // a few per cent)
+    const int tiles_m64 = (M + 63) / 64;
+    const int64_t T64 = (int64_t)tiles_m64 * tiles_n;
+    if (T64 <= kCUs / 2) {
+        hipLaunchKernelGGL((k_gemm<FMT, 1, 64>), dim3((unsigned)(4 * T64)), dim3(256), 0, s, X, Wp, scale, M, N, K, C,
+                           tiles_m64, tiles_n, 0, Y);
         return hipGetLastError() == hipSuccess ? TRI_OK : TRI_EHIP;
     }
     // A last round of full tiles that would leave more than half of the CUs idle is run as
@@ -364,10 +370,10 @@ static int launch_fmt(const uint16_t *X, const uint8_t *Wp, float scale, int M, 
     const int tail = (r > 0 && r <= kCUs / 2) ? r : 0;
     const int full = (int)T - tail;
     if (full > 0)
-        hipLaunchKernelGGL((k_gemm<FMT, 4>), dim3((unsigned)full), dim3(256), 0, s, X, Wp, scale, M, N, K, C, tiles_m,
+        hipLaunchKernelGGL((k_gemm<FMT, 4, 128>), dim3((unsigned)full), dim3(256), 0, s, X, Wp, scale, M, N, K, C, tiles_m,
                            tiles_n, 0, Y);
     if (tail > 0)
-        hipLaunchKernelGGL((k_gemm<FMT, 2>), dim3((unsigned)(2 * tail)), dim3(256), 0, s, X, Wp, scale, M, N, K, C,
+        hipLaunchKernelGGL((k_gemm<FMT, 2, 128>), dim3((unsigned)(2 * tail)), dim3(256), 0, s, X, Wp, scale, M, N, K, C,
                            tiles_m, tiles_n, full, Y);
     return hipGetLastError() == hipSuccess ? TRI_OK : TRI_EHIP;
 }

@@ -50,22 +50,21 @@ def test_select_algo():
     assert tri.tri_select_algo(1, 4096, 4096, F2) == tri.TRI_ALGO_SMALLM   # the MFMA kernel also serves M = 1
     assert tri.tri_select_algo(1, 4096, 4096, F16) == tri.TRI_ALGO_SMALLM
     assert tri.tri_select_algo(16, 4096, 4096, F2) == tri.TRI_ALGO_SMALLM
-    # above 16 rows, the cheaper of the two by the fitted cost model (crossovers measured on MI355X)
-    assert tri.tri_select_algo(17, 4096, 4096, F2) == tri.TRI_ALGO_SMALLM
-    assert tri.tri_select_algo(256, 4096, 4096, F2) == tri.TRI_ALGO_SMALLM
-    assert tri.tri_select_algo(384, 4096, 4096, F2) == tri.TRI_ALGO_GEMM
-    assert tri.tri_select_algo(96, 11008, 4096, F2) == tri.TRI_ALGO_SMALLM
-    assert tri.tri_select_algo(128, 11008, 4096, F2) == tri.TRI_ALGO_GEMM
-    assert tri.tri_select_algo(256, 4096, 11008, F2) == tri.TRI_ALGO_SMALLM
-    assert tri.tri_select_algo(384, 4096, 11008, F2) == tri.TRI_ALGO_GEMM
-    assert tri.tri_select_algo(32, 28672, 8192, F2) == tri.TRI_ALGO_SMALLM
-    assert tri.tri_select_algo(48, 28672, 8192, F2) == tri.TRI_ALGO_GEMM
-    assert tri.tri_select_algo(64, 8192, 28672, F2) == tri.TRI_ALGO_SMALLM    # rows past eight steps per wave
-    assert tri.tri_select_algo(128, 8192, 28672, F2) == tri.TRI_ALGO_GEMM
-    assert tri.tri_select_algo(64, 8192, 28672, F16) == tri.TRI_ALGO_SMALLM
-    assert tri.tri_select_algo(128, 8192, 28672, F16) == tri.TRI_ALGO_GEMM
-    assert tri.tri_select_algo(2048, 28672, 8192, F2) == tri.TRI_ALGO_GEMM
-    assert tri.tri_select_algo(2048, 8192, 28672, F16) == tri.TRI_ALGO_GEMM
+    # above 16 rows, the cheaper of the two by the fitted cost model; each pair brackets a crossover measured on
+    # MI355X, on points where the faster of the two won by at least 15%
+    S, G = tri.TRI_ALGO_SMALLM, tri.TRI_ALGO_GEMM
+    for M, N, K, f, want in [
+            (17, 4096, 4096, F2, S), (128, 4096, 4096, F2, S), (384, 4096, 4096, F2, G),
+            (128, 4096, 4096, F16, S), (256, 4096, 4096, F16, G),
+            (48, 11008, 4096, F2, S), (96, 11008, 4096, F2, G),          # 64-row GEMM tiles at a middling M
+            (32, 11008, 4096, F16, S), (96, 11008, 4096, F16, G),
+            (128, 4096, 11008, F2, S), (192, 4096, 11008, F2, G),
+            (128, 4096, 11008, F16, S), (256, 4096, 11008, F16, G),
+            (17, 28672, 8192, F2, G), (17, 28672, 8192, F16, G),
+            (32, 8192, 28672, F2, S), (64, 8192, 28672, F2, G),          # rows past eight steps per wave
+            (48, 8192, 28672, F16, S), (96, 8192, 28672, F16, G),
+            (2048, 28672, 8192, F2, G), (2048, 8192, 28672, F16, G)]:
+        assert tri.tri_select_algo(M, N, K, f) == want, (M, N, K, f)
     assert tri.tri_select_algo(0, 4096, 4096, F2) == tri.TRI_EINVAL
     assert tri.tri_select_algo(1, 4096, 4096, 3) == tri.TRI_EINVAL
 
