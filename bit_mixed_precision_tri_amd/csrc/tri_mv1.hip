@@ -63,12 +63,18 @@ __device__ __forceinline__ float4_t mfma(const u32x4 a, const u32x4 b, float4_t 
 
 }  // namespace
 
-template <int FMT, int NW, int CST, int GL, bool ONE, int MR, int RB>
+// Block loop: outputs held in LDS before they are written (an even count), and the blocks per
+// resident workgroup slot from which the loop pays.
+constexpr int kPsOut = 16;
+constexpr int kLoopBlocksPerSlot = 2;
+
+template <int FMT, int NW, int CST, int GL, bool ONE, int MR, int RB, bool PS>
 __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X, const Groups gr, int M, int K, int C,
                                                  const Fusion fu)
 {
     static_assert(MR == 1 || ((MR == 2 || MR == 4) && GL == 0), "several activation rows: the plain layer (and the residual) only");
     static_assert(RB == 1 || GL == 0, "several row blocks: the plain layer (and the residual) only");
+    static_assert(!PS || (GL == 0 && RB == 1 && ONE), "block loop: one matrix, the plain layer (and the residual) only");
     constexpr bool NORM = (GL & kGlueNorm) != 0;
     constexpr bool PAIR = (GL & kGluePair) != 0;
     const GroupSel grp = select_group<ONE>(gr, fu, (int)blockIdx.x);
@@ -87,7 +93,8 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
     __shared__ u32x4 xa[NW][NCH][MR][NOP];       // per wave: A operands of its chunks, per activation row
     __shared__ u32x4 xraw[TWO ? 1 : NW][TWO ? 1 : NCH * PIECES];   // 1.6-bit: raw pieces
     // per wave and activation row: the 16 outputs of each block, sum x (, sum x^2)
-    __shared__ float red[NW][MR][16 * RB + (NORM ? 2 : 1)];
+    __shared__ float red[PS ? 2 : 1][NW][MR][16 * RB + (NORM ? 2 : 1)];   // (block loop: two, alternating)
+    __shared__ float yst[PS ? kPsOut : 1][MR][16];   // block loop: outputs not yet written
     __shared__ float red1[PAIR ? NW : 1][16];    // pair: the second matrix's rows
 
     const int lane = threadIdx.x & 63;
@@ -118,23 +125,35 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
                 if (fu.gain) nv[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc(fu.gain, (uint32_t)K * 2u), off, 0, 0);
             }
         }
-    // (2) every weight chunk of the wave, all in flight at once
-    const int rows_here = min(16 * RB, N - n0);
+    // (2) every weight chunk of the wave, all in flight at once.  Block loop (PS): the workgroup
+    //     takes blocks blockIdx.x, + gridDim.x, ...; one resource spans the matrix, and the chunks
+    //     of a block past its end read as zero
+    const int rows_here = PS ? N : min(16 * RB, N - n0);
     const __amdgpu_buffer_rsrc_t wr =
-        rsrc(Wp + (int64_t)n0 * S, __builtin_amdgcn_readfirstlane((uint32_t)(rows_here * S)));
+        rsrc(Wp + (PS ? 0 : (int64_t)n0 * S), __builtin_amdgcn_readfirstlane((uint32_t)(rows_here * S)));
     // (pair: the same chunks of the second matrix, requested in the order they are used)
     const __amdgpu_buffer_rsrc_t wr1 =
         rsrc(gr.Wp[PAIR ? 1 : 0] + (int64_t)n0 * S, __builtin_amdgcn_readfirstlane((uint32_t)(rows_here * S)));
-    u32x4 wq[RB][CST], wq1[PAIR ? CST : 1];
+    const int nblk = (N + 15) / 16;
+    auto load_block = [&](int b, u32x4 (&w)[RB][CST]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int s = 0; s < CST; ++s) {
-        const int c = 4 * (s * NW + wv) + g;
-        const int off = c < C ? (int)(uint32_t)(j * S + c * 16) : (int)0x80000000u;
+        for (int s = 0; s < CST; ++s) {
+            const int c = 4 * (s * NW + wv) + g;
+            const bool live = c < C && (!PS || b < nblk);
 #pragma unroll
-        for (int r = 0; r < RB; ++r)             // (rows past the matrix's end read as zero)
-            wq[r][s] = __builtin_amdgcn_raw_buffer_load_b128(
-                wr, c < C ? (int)(uint32_t)((16 * r + j) * S + c * 16) : (int)0x80000000u, 0, 0);
-        if constexpr (PAIR) wq1[s] = __builtin_amdgcn_raw_buffer_load_b128(wr1, off, 0, 0);
+            for (int r = 0; r < RB; ++r)         // (rows past the matrix's end read as zero)
+                w[r][s] = __builtin_amdgcn_raw_buffer_load_b128(
+                    wr, live ? (int)(uint32_t)((16 * (PS ? b : r) + j) * S + c * 16) : (int)0x80000000u, 0, 0);
+        }
+    };
+    u32x4 wq[RB][CST], wq1[PAIR ? CST : 1], wqb[PS ? RB : 1][PS ? CST : 1];
+    load_block((int)blockIdx.x, wq);
+    if constexpr (PAIR) {
+#pragma unroll
+        for (int s = 0; s < CST; ++s) {
+            const int c = 4 * (s * NW + wv) + g;
+            wq1[s] = __builtin_amdgcn_raw_buffer_load_b128(wr1, c < C ? (int)(uint32_t)(j * S + c * 16) : (int)0x80000000u, 0, 0);
+        }
     }
 
     // (3) norm: sum of squares, then x -> fp16(x * gain); A operands in LDS and this lane's
@@ -227,13 +246,6 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
 
     // (4) decode and contract, one MFMA per position (and half, 1.6-bit)
     const float4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-    float4_t acc[RB][NCLS], acc1[PAIR ? NCLS : 1];
-#pragma unroll
-    for (int r = 0; r < RB; ++r)
-#pragma unroll
-        for (int c = 0; c < NCLS; ++c) acc[r][c] = zero4;
-#pragma unroll
-    for (int c = 0; c < (PAIR ? NCLS : 1); ++c) acc1[c] = zero4;
     auto contract = [&](const u32x4 (&a)[NOP], const u32x4 v, float4_t (&ac)[NCLS]) __attribute__((always_inline)) {
         if constexpr (TWO) {
             const u32x4 u = v >> 12u;
@@ -254,18 +266,6 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
             }
         }
     };
-#pragma unroll
-    for (int s = 0; s < CST; ++s) {
-        if (4 * (s * NW + wv) >= C) break;       // wave-uniform: no chunk of this step is live
-        const u32x4 *asrc = &xa[wv][4 * s + g][j % MR][0];   // A row j: activation row j % MR
-        u32x4 a[NOP];
-#pragma unroll
-        for (int p = 0; p < NOP; ++p) a[p] = asrc[p];
-#pragma unroll
-        for (int r = 0; r < RB; ++r) contract(a, wq[r][s], acc[r]);
-        if constexpr (PAIR) contract(a, wq1[s], acc1);
-    }
-
     // (5) merge classes (D row i holds activation row i % MR; rows 0..MR-1 are elements 0..MR-1
     //     of lanes 0..15), add the waves' partial sums in a fixed order, subtract sum_k x, scale,
     //     round
@@ -277,51 +277,125 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
         return t;
     };
     const float xs_wave = wave_reduce_rows<MR>(xsum, lane);   // lane group r (of 64 / MR lanes): row r
-#pragma unroll
-    for (int r = 0; r < RB; ++r) {
-        const float4_t t = merge(acc[r]);
-        if (g == 0) {
-#pragma unroll
-            for (int e = 0; e < MR; ++e) red[wv][e][16 * r + j] = t[e];
-        }
-    }
-    if ((lane & (64 / MR - 1)) == 0) red[wv][lane / (64 / MR)][16 * RB] = xs_wave;
-    if constexpr (PAIR) {
-        const float4_t t1 = merge(acc1);
-        if (g == 0) red1[wv][j] = t1[0];
-    }
+    float xq_wave = 0.f;
     if constexpr (NORM) {
         float xq[1] = {xsq};
-        const float xq_wave = wave_reduce_rows<1>(xq, lane);
-        if (lane == 0) red[wv][0][16 * RB + 1] = xq_wave;
+        xq_wave = wave_reduce_rows<1>(xq, lane);
     }
-    __syncthreads();
-    const int e = threadIdx.x / (16 * RB), jj = threadIdx.x % (16 * RB);   // thread (e, jj): output Y[e][n0 + jj]
-    if (threadIdx.x < 16 * RB * MR && e < M && n0 + jj < N) {
-        float sd = 0.f, sx = 0.f;
+    // steps (4) and (5) for the blocks whose weight chunks are in w, the first at row nb, through
+    // partial-sum buffer rbuf
+    auto run = [&](const u32x4 (&w)[RB][CST], int nb, int rbuf, int slot) __attribute__((always_inline)) {
+        float4_t acc[RB][NCLS], acc1[PAIR ? NCLS : 1];
 #pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            sd += red[w][e][jj];
-            sx += red[w][e][16 * RB];
-        }
-        float rinv = 1.f;
-        if constexpr (NORM) {
-            float sq = 0.f;
+        for (int r = 0; r < RB; ++r)
 #pragma unroll
-            for (int w = 0; w < NW; ++w) sq += red[w][0][16 * RB + 1];
-            rinv = 1.f / sqrtf(sq / (float)K + fu.eps);
+            for (int c = 0; c < NCLS; ++c) acc[r][c] = zero4;
+#pragma unroll
+        for (int c = 0; c < (PAIR ? NCLS : 1); ++c) acc1[c] = zero4;
+#pragma unroll
+        for (int s = 0; s < CST; ++s) {
+            // wave-uniform: no chunk of this step is live (the block loop contracts such steps,
+            // whose activations are zero: a skipped step would leave its loads pending)
+            if (!PS && 4 * (s * NW + wv) >= C) break;
+            const u32x4 *asrc = &xa[wv][4 * s + g][j % MR][0];   // A row j: activation row j % MR
+            u32x4 a[NOP];
+#pragma unroll
+            for (int p = 0; p < NOP; ++p) a[p] = asrc[p];
+#pragma unroll
+            for (int r = 0; r < RB; ++r) contract(a, w[r][s], acc[r]);
+            if constexpr (PAIR) contract(a, wq1[s], acc1);
         }
-        float y = (sd * 16777216.0f - sx) * scale * rinv;
+        auto &rd = red[rbuf];
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            const float4_t t = merge(acc[r]);
+            if (g == 0) {
+#pragma unroll
+                for (int e = 0; e < MR; ++e) rd[wv][e][16 * r + j] = t[e];
+            }
+        }
+        if ((lane & (64 / MR - 1)) == 0) rd[wv][lane / (64 / MR)][16 * RB] = xs_wave;
         if constexpr (PAIR) {
-            float sd1 = 0.f;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) sd1 += red1[w][jj];
-            const float y1 = (sd1 * 16777216.0f - sx) * gr.scale[1] * rinv;
-            y = y / (1.f + __expf(-y)) * y1;     // silu(gate) * up
+            const float4_t t1 = merge(acc1);
+            if (g == 0) red1[wv][j] = t1[0];
         }
-        const int64_t o = (int64_t)e * N + n0 + jj;
-        if (grp.res) y += h2f(grp.res[o]);
-        Y[o] = __builtin_bit_cast(uint16_t, (_Float16)y);
+        if constexpr (NORM) {
+            if (lane == 0) rd[wv][0][16 * RB + 1] = xq_wave;
+        }
+        __syncthreads();
+        const int e = threadIdx.x / (16 * RB), jj = threadIdx.x % (16 * RB);   // thread (e, jj): output Y[e][nb + jj]
+        if (threadIdx.x < 16 * RB * MR && e < M && nb + jj < N) {
+            float sd = 0.f, sx = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                sd += rd[w][e][jj];
+                sx += rd[w][e][16 * RB];
+            }
+            float rinv = 1.f;
+            if constexpr (NORM) {
+                float sq = 0.f;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) sq += rd[w][0][16 * RB + 1];
+                rinv = 1.f / sqrtf(sq / (float)K + fu.eps);
+            }
+            float y = (sd * 16777216.0f - sx) * scale * rinv;
+            if constexpr (PAIR) {
+                float sd1 = 0.f;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) sd1 += red1[w][jj];
+                const float y1 = (sd1 * 16777216.0f - sx) * gr.scale[1] * rinv;
+                y = y / (1.f + __expf(-y)) * y1;     // silu(gate) * up
+            }
+            if constexpr (PS) {
+                yst[slot][e][jj] = y;            // (written out by the flush below)
+            } else {
+                const int64_t o = (int64_t)e * N + nb + jj;
+                if (grp.res) y += h2f(grp.res[o]);
+                Y[o] = __builtin_bit_cast(uint16_t, (_Float16)y);
+            }
+        }
+    };
+    if constexpr (!PS) {
+        run(wq, n0, 0, 0);
+    } else {
+        // Two register sets in turn: the next block's chunks are in flight while one is
+        // contracted, and the two partial-sum buffers alternate, so one barrier per block
+        // suffices.  Outputs wait in LDS and are written kPsOut blocks at a time, away from the
+        // loads in flight.
+        const int G = (int)gridDim.x;
+        int done = 0;                            // blocks of this workgroup whose outputs are written
+        auto flush = [&](int upto) __attribute__((always_inline)) {
+            __syncthreads();
+            for (int t = (int)threadIdx.x; t < (upto - done) * MR * 16; t += 64 * NW) {
+                const int i = t / (MR * 16), e = (t / 16) % MR, jj = t % 16;
+                const int n = 16 * ((int)blockIdx.x + (done + i) * G) + jj;
+                if (e < M && n < N) {
+                    const int64_t o = (int64_t)e * N + n;
+                    float y = yst[i][e][jj];
+                    if (grp.res) y += h2f(grp.res[o]);
+                    Y[o] = __builtin_bit_cast(uint16_t, (_Float16)y);
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no store stays pending into the loop
+            __syncthreads();
+            done = upto;
+        };
+        // (The exit between the two halves costs a drain of the loads in flight at the top of
+        // the loop, which the compiler inserts; contracting a phantom block past the matrix
+        // instead measured slower.)
+        int i = 0;                               // blocks of this workgroup contracted
+        for (int b = (int)blockIdx.x; b < nblk; b += 2 * G, i += 2) {
+            load_block(b + G, wqb);
+            run(wq, 16 * b, 0, i - done);
+            if (b + G >= nblk) {
+                ++i;
+                break;
+            }
+            load_block(b + 2 * G, wq);
+            run(wqb, 16 * (b + G), 1, i + 1 - done);
+            if (i + 2 - done == kPsOut) flush(i + 2);
+        }
+        flush(i);
     }
 }
 
@@ -336,10 +410,28 @@ static bool launch_gl(const uint16_t *X, const Groups &gr, int M, int K, int C, 
     } else {
         const Groups g = RB == 1 ? gr : regroup(gr, RB);
         const dim3 grid(g.blk[g.G]), block(64 * NW);
+        if constexpr (GL == 0 && RB == 1 && NW <= 8) {
+            // one matrix of many blocks: a resident grid that loops over the blocks (sixteen waves
+            // would spill the second register set)
+            if (g.G == 1 && (int64_t)gr.N[0] * C * 16 < ((int64_t)1 << 31)) {
+                static const int resident = [] {
+                    int n = 0;
+                    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_mv1<FMT, NW, CST, 0, true, MR, 1, true>,
+                                                                     64 * NW, 0) != hipSuccess || n < 1)
+                        n = 1;
+                    return n * kCUs;
+                }();
+                if ((int64_t)g.blk[1] >= (int64_t)kLoopBlocksPerSlot * resident) {
+                    hipLaunchKernelGGL((k_mv1<FMT, NW, CST, 0, true, MR, 1, true>), dim3(resident), block, 0, s, X, g,
+                                       M, K, C, f);
+                    return true;
+                }
+            }
+        }
         if (g.G == 1)
-            hipLaunchKernelGGL((k_mv1<FMT, NW, CST, GL, true, MR, RB>), grid, block, 0, s, X, g, M, K, C, f);
+            hipLaunchKernelGGL((k_mv1<FMT, NW, CST, GL, true, MR, RB, false>), grid, block, 0, s, X, g, M, K, C, f);
         else
-            hipLaunchKernelGGL((k_mv1<FMT, NW, CST, GL, false, MR, RB>), grid, block, 0, s, X, g, M, K, C, f);
+            hipLaunchKernelGGL((k_mv1<FMT, NW, CST, GL, false, MR, RB, false>), grid, block, 0, s, X, g, M, K, C, f);
         return true;
     }
 }
