@@ -99,6 +99,22 @@ __device__ __forceinline__ void base3_digits_u16x2(uint32_t b, uint32_t (&d)[5])
     d[4] = __builtin_bit_cast(uint32_t, q4);
 }
 
+// The quotients q_j = floor(b / 3^j), j = 0..4, of two bytes at once (q_0 = b), by the same
+// multiply-shifts.  Since d_j = q_j - 3 q_{j+1} (q_5 = 0), a dot product with the digits is
+//   sum_j x_j d_j = sum_j x_j q_j - 3 sum_{j<4} x_j q_{j+1},
+// two dot products with the quotients, which saves the four multiply-subtracts of the digits.
+// Every quotient is below 2^8, so its bits read as fp16 are the exact value q * 2^-24.
+__device__ __forceinline__ void base3_quotients_u16x2(uint32_t b, uint32_t (&q)[5])
+{
+    typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+    const u16x2 v = __builtin_bit_cast(u16x2, b);
+    q[0] = b;
+    q[1] = __builtin_bit_cast(uint32_t, (u16x2)((v * (uint16_t)171) >> (uint16_t)9));
+    q[2] = __builtin_bit_cast(uint32_t, (u16x2)((v * (uint16_t)57) >> (uint16_t)9));
+    q[3] = __builtin_bit_cast(uint32_t, (u16x2)((v * (uint16_t)19) >> (uint16_t)9));
+    q[4] = __builtin_bit_cast(uint32_t, (u16x2)((v * (uint16_t)203) >> (uint16_t)14));
+}
+
 // Bytes q and q + 8 (q < 8) of a 16-byte chunk as the two 16-bit lanes of one register.
 __device__ __forceinline__ uint32_t byte_pair(const u32x4 v, int q)
 {

@@ -85,7 +85,7 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
     constexpr bool TWO = FMT == TRI_FMT_2BIT;
     constexpr int XH = TWO ? 64 : 80;            // activations per chunk
     constexpr int NOP = TWO ? 8 : 10;            // A operands (MFMAs) per chunk
-    constexpr int NCLS = TWO ? 6 : 2;            // accumulators: position classes (2-bit), halves (1.6-bit)
+    constexpr int NCLS = TWO ? 6 : 4;            // accumulators: position classes (2-bit); two sums by halves (1.6-bit)
     constexpr int NCH = 4 * CST;                 // chunks per wave
     constexpr int PIECES = XH / 8;               // 16-byte activation pieces per chunk
     constexpr int NLD = (NCH * PIECES + 63) / 64;   // whole-line activation loads per lane
@@ -254,15 +254,20 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
             ac[0] = mfma(a[6], u & 0x00030003u, ac[0]);
             ac[1] = mfma(a[7], u & 0x000C000Cu, ac[1]);
         } else {
-            // register q: bytes q and q+8, position p pairs trits (5q+p, 5q+40+p); every digit
-            // carries the same scale, so the halves accumulate in ac[0] and ac[1]
-            uint32_t dg[8][5];
+            // register q: bytes q and q+8, position p pairs trits (5q+p, 5q+40+p).  From the
+            // quotients q_p of the bytes: ac[0], ac[1] gather sum x_p q_p and ac[2], ac[3]
+            // sum x_p q_{p+1}, by halves (every quotient carries the same scale)
+            uint32_t qt[8][5];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) base3_digits_u16x2(byte_pair(v, q), dg[q]);
+            for (int q = 0; q < 8; ++q) base3_quotients_u16x2(byte_pair(v, q), qt[q]);
 #pragma unroll
             for (int p = 0; p < 5; ++p) {
-                ac[0] = mfma(a[2 * p], u32x4{dg[0][p], dg[1][p], dg[2][p], dg[3][p]}, ac[0]);
-                ac[1] = mfma(a[2 * p + 1], u32x4{dg[4][p], dg[5][p], dg[6][p], dg[7][p]}, ac[1]);
+                ac[0] = mfma(a[2 * p], u32x4{qt[0][p], qt[1][p], qt[2][p], qt[3][p]}, ac[0]);
+                ac[1] = mfma(a[2 * p + 1], u32x4{qt[4][p], qt[5][p], qt[6][p], qt[7][p]}, ac[1]);
+                if (p < 4) {
+                    ac[2] = mfma(a[2 * p], u32x4{qt[0][p + 1], qt[1][p + 1], qt[2][p + 1], qt[3][p + 1]}, ac[2]);
+                    ac[3] = mfma(a[2 * p + 1], u32x4{qt[4][p + 1], qt[5][p + 1], qt[6][p + 1], qt[7][p + 1]}, ac[3]);
+                }
             }
         }
     };
@@ -270,7 +275,7 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
     //     of lanes 0..15), add the waves' partial sums in a fixed order, subtract sum_k x, scale,
     //     round
     auto merge = [&](const float4_t (&ac)[NCLS]) __attribute__((always_inline)) {
-        if constexpr (!TWO) return ac[0] + ac[1];
+        if constexpr (!TWO) return (ac[0] + ac[1]) - 3.f * (ac[2] + ac[3]);   // digits d_p = q_p - 3 q_{p+1}
         float4_t t = ac[0] + 0.25f * ac[1];
         t += 0.0625f * ac[2] + 0.015625f * ac[3];
         t += 0.00390625f * ac[4] + 0.0009765625f * ac[5];

@@ -75,7 +75,11 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
     constexpr bool TWO = FMT == TRI_FMT_2BIT;
     constexpr int XH = TWO ? 64 : 80;            // activations per chunk
     constexpr int NOP = TWO ? 8 : 10;            // A operands (MFMAs) per chunk
-    constexpr int NCLS = TWO ? 6 : 2;            // accumulators: position classes (2-bit), halves (1.6-bit)
+    // 1.6-bit from base-3 quotients (two sums by halves) where the registers allow it and
+    // the tile has rows enough to keep the matrix cores' extra work off the critical path (at
+    // four rows it measured slower); from the digits (one sum by halves) otherwise
+    constexpr bool QT = !TWO && MT >= 8 && CST < 14;   // (not RB: grouped and single launches agree bitwise)
+    constexpr int NCLS = TWO ? 6 : (QT ? 4 : 2);   // accumulators: position classes (2-bit), sums (1.6-bit)
     constexpr int RP = 4 * XH / 8;               // 16-byte pieces of one row per step (32 or 40)
     constexpr int NLD = (MT * RP + 63) / 64;     // whole-line activation loads per lane and step
     constexpr int RPP = RP + 1;                  // padded row stride: the 16 rows a read touches fall in distinct banks
@@ -137,15 +141,24 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
             ac[0] = mfma(a[6], u & 0x00030003u, ac[0]);
             ac[1] = mfma(a[7], u & 0x000C000Cu, ac[1]);
         } else {
-            // register q: bytes q and q+8, position p pairs trits (5q+p, 5q+40+p); every digit
-            // carries the same scale, so the halves accumulate in ac[0] and ac[1]
-            uint32_t dg[8][5];
+            // register q: bytes q and q+8, position p pairs trits (5q+p, 5q+40+p).  From the
+            // quotients q_p of the bytes: ac[0], ac[1] gather sum x_p q_p and ac[2], ac[3]
+            // sum x_p q_{p+1}, by halves; from the digits: ac[0], ac[1] gather sum x_p d_p (every
+            // quotient and digit carries the same scale)
+            uint32_t qt[8][5];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) base3_digits_u16x2(byte_pair(v, q), dg[q]);
+            for (int q = 0; q < 8; ++q) {
+                if constexpr (QT) base3_quotients_u16x2(byte_pair(v, q), qt[q]);
+                else base3_digits_u16x2(byte_pair(v, q), qt[q]);
+            }
 #pragma unroll
             for (int p = 0; p < 5; ++p) {
-                ac[0] = mfma(a[2 * p], u32x4{dg[0][p], dg[1][p], dg[2][p], dg[3][p]}, ac[0]);
-                ac[1] = mfma(a[2 * p + 1], u32x4{dg[4][p], dg[5][p], dg[6][p], dg[7][p]}, ac[1]);
+                ac[0] = mfma(a[2 * p], u32x4{qt[0][p], qt[1][p], qt[2][p], qt[3][p]}, ac[0]);
+                ac[1] = mfma(a[2 * p + 1], u32x4{qt[4][p], qt[5][p], qt[6][p], qt[7][p]}, ac[1]);
+                if (QT && p < 4) {
+                    ac[NCLS - 2] = mfma(a[2 * p], u32x4{qt[0][p + 1], qt[1][p + 1], qt[2][p + 1], qt[3][p + 1]}, ac[NCLS - 2]);
+                    ac[NCLS - 1] = mfma(a[2 * p + 1], u32x4{qt[4][p + 1], qt[5][p + 1], qt[6][p + 1], qt[7][p + 1]}, ac[NCLS - 1]);
+                }
             }
         }
     };
@@ -243,7 +256,10 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
 
     // merge classes: lane (g, j) holds rows 4g + e of column j (of D and of the sums of X)
     auto merge = [&](const float4_t (&ac)[NCLS]) __attribute__((always_inline)) {
-        if constexpr (!TWO) return ac[0] + ac[1];
+        if constexpr (!TWO) {
+            if constexpr (QT) return (ac[0] + ac[1]) - 3.f * (ac[NCLS - 2] + ac[NCLS - 1]);   // d_p = q_p - 3 q_{p+1}
+            else return ac[0] + ac[1];
+        }
         float4_t t = ac[0] + 0.25f * ac[1];
         t += 0.0625f * ac[2] + 0.015625f * ac[3];
         t += 0.00390625f * ac[4] + 0.0009765625f * ac[5];
@@ -323,8 +339,10 @@ constexpr bool has_rb()
     if (GL & kGluePair) return false;
     const int c = CST + ((GL & kGlueNorm) ? 1 : 0);   // the norm takes about one more step's registers
     if (RB == 2) return FMT == TRI_FMT_2BIT ? (MT == 16 ? c <= 6 : c <= 8) : (MT == 16 ? c <= 5 : c <= 6);
-    // (1.6-bit tiles of 4 rows: four blocks measured 4% slower than two)
-    if (RB == 4) return MT == 16 ? c <= 3 : MT == 8 ? c <= 4 : (FMT == TRI_FMT_2BIT && c <= 5);
+    // (1.6-bit tiles of 4 rows: four blocks measured 4% slower than two; of 8 rows, the
+    // quotient accumulators take one step's registers)
+    if (RB == 4)
+        return MT == 16 ? c <= 3 : MT == 8 ? c <= (FMT == TRI_FMT_2BIT ? 4 : 3) : (FMT == TRI_FMT_2BIT && c <= 5);
     return false;
 }
 
