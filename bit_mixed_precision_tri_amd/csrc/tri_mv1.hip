@@ -18,11 +18,14 @@
 // sum_k d*x; since t = d - 1, sum_k x is subtracted once per row at the end.
 //   2-bit:   a register pairs trits (16v+p, 16v+8+p); positions 6, 7 are taken from the
 //            word shifted right by 12, so they share the classes of 0 and 1.
-//   1.6-bit: bytes q and q+8 of a chunk become the two 16-bit lanes of a register, whose five
-//            base-3 digits (the repeated division b'_i -> x_i that the review's referee report
-//            describes for the paper's section 3.2) come from exact multiply-shift quotients,
-//            one digit per lane and register: position p pairs trits (5q+p, 5q+40+p), and every
-//            digit reads as d * 2^-24, so the two halves of a chunk need one accumulator each.
+//   1.6-bit: bytes q and q+8 of a chunk become the two 16-bit lanes of a register.  Their
+//            base-3 digits are d_p = q_p - 3 q_{p+1} with q_p = floor(b / 3^p) (the repeated
+//            division b'_i -> x_i that the review's referee report describes for the paper's
+//            section 3.2), each quotient an exact multiply-shift; position p pairs trits
+//            (5q+p, 5q+40+p).  The kernel contracts the quotients, not the digits:
+//            sum_p x_p d_p = sum_p x_p q_p - 3 sum_p x_p q_{p+1}, two MFMA sums (each by halves
+//            of the chunk) whose every quotient reads as q * 2^-24; that spares the VALU, which
+//            bounds this format, four multiply-subtracts per register.
 // The sum over k is order-free, so the activations are permuted into the same pairing.
 //
 // Work split.  A workgroup of NW waves owns 16 weight rows; wave w takes chunk-steps s,

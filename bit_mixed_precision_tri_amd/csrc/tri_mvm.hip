@@ -7,9 +7,10 @@
 // v_mfma_f32_16x16x32_f16 takes the (up to) 16 activation rows as its A operand and 16 weight
 // rows, decoded in registers, as B.  The decode is the one of the M = 1 kernel (tri_mv1.hip):
 // digits d = t + 1 read as exact fp16 values (2-bit: masked in place, d * 4^p * 2^-24, one
-// accumulator per position class, merged with exact powers of two; 1.6-bit: base-3 digits
-// from multiply-shift quotients, d * 2^-24, one accumulator per half chunk), and
-// sum_k X[m][k] subtracted once per output at the end.
+// accumulator per position class, merged with exact powers of two; 1.6-bit: the base-3
+// quotients q_p, q * 2^-24, in two sums sum x_p q_p - 3 sum x_p q_{p+1} for tiles of 8 and 16
+// rows, the digits d_p = q_p - 3 q_{p+1} themselves for tiles of 4 rows and the longest rows),
+// and sum_k X[m][k] subtracted once per output at the end.
 //
 // Work split.  A workgroup of NW waves owns RB blocks of 16 weight rows; wave w takes chunk-steps
 // s, where lane (g = lane/16, j = lane%16) reads 16-byte chunk c = 4*(s*NW + w) + g of row j of
