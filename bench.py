@@ -332,6 +332,7 @@ def main():
     }
     if not args.skip_extra:
         out["decode_1p6bit"] = bench_decode_1p6(clock)
+        out["decode_large"] = bench_decode_large(clock)
         out["batched"] = bench_batched(clock)
         out["mid_m"] = bench_mid_m(clock)
         out["block"] = bench_block(clock)
@@ -380,9 +381,32 @@ def bench_mid_m(clock):
     return res
 
 
+def bench_decode_large(clock):
+    """Decode (M = 1, 2) on the 58.7 MB (2-bit) prefill matrices, cold weights (eight copies,
+    beyond the last-level cache), with the size-matched read floor of the packed bytes."""
+    import torch
+    import bit_mixed_precision_tri_amd as tri
+    from bit_mixed_precision_tri_amd import configs
+    cfg = configs.DECODE_LARGE
+    res = []
+    for fmt in cfg["fmts"]:
+        for li, (name, K, N) in enumerate(cfg["shapes"]):
+            nb = N * tri.tri_row_bytes(K, fmt)
+            tf = read_floor(nb, clock)
+            for M in cfg["Ms"]:
+                L = Layer(cfg["workload_id"], 10 * li + M, M, N, K, fmt, copies=8)
+                t, _ = clock.run([L.launch] * 100)
+                res.append({"shape": name, "M": M, "format": configs.FMT_NAMES[fmt], "kernel_us": round(t * 1e6, 3),
+                            "GBps": round(L.bytes / t / 1e9, 1), "frac_hbm": round(L.bytes / t / 1e9 / HBM_PEAK_GBS, 4),
+                            "read_floor_us": round(tf * 1e6, 3), "read_floor_over_kernel": round(tf / t, 3)})
+                del L
+                torch.cuda.empty_cache()
+    return res
+
+
 def bench_decode_1p6(clock):
-    """The decode shapes at M = 1 with 1.6-bit packed weights (k_mv1, base-3 digits through the LDS
-    byte table), cold weights; with the size-matched read floor of the 1.6-bit bytes."""
+    """The decode shapes at M = 1 with 1.6-bit packed weights (k_mv1, base-3 quotients by
+    multiply-shift), cold weights; with the size-matched read floor of the 1.6-bit bytes."""
     import torch
     import bit_mixed_precision_tri_amd as tri
     from bit_mixed_precision_tri_amd import configs

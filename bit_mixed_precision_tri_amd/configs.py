@@ -29,6 +29,12 @@ BATCHED = dict(workload_id=3, Ms=(4, 8, 16),
 MID_M = dict(workload_id=6, Ms=(32, 64, 128, 256),
              shapes=[("gate_up_4096to11008", 4096, 11008), ("down_11008to4096", 11008, 4096)], fmt=FMT_2BIT)
 
+# workload 7: decode on the prefill matrices (a 70B-class MLP, 58.7 MB packed 2-bit per
+# matrix), M in {1, 2}, both formats: launches long enough for the streaming rate to dominate
+DECODE_LARGE = dict(workload_id=7, Ms=(1, 2),
+                    shapes=[("up_8192to28672", 8192, 28672), ("down_28672to8192", 28672, 8192)],
+                    fmts=(FMT_2BIT, FMT_1P6BIT))
+
 # workload 4: one LLaMA-style block decode step (seven ternary linears), M in {1, 8}
 BLOCK_LAYERS = [  # (name, K, N)
     ("q", 4096, 4096), ("k", 4096, 4096), ("v", 4096, 4096), ("o", 4096, 4096),
