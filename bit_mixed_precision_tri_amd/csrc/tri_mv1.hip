@@ -411,9 +411,9 @@ template <int FMT, int NW, int CST, int GL, int MR, int RB>
 static bool launch_gl(const uint16_t *X, const Groups &gr, int M, int K, int C, hipStream_t s, const Fusion &f)
 {
     // several activation rows: only while the staged A operands of the workgroup stay below
-    // 100 KB of LDS
+    // 100 KB of LDS (136 KB at sixteen waves, whose registers hold one workgroup per CU anyway)
     constexpr int kXaBytes = NW * 4 * CST * MR * (FMT == TRI_FMT_2BIT ? 8 : 10) * 16;
-    if constexpr (MR > 1 && kXaBytes > 100 * 1024) {
+    if constexpr (MR > 1 && kXaBytes > (NW == 16 ? 136 : 100) * 1024) {
         return false;
     } else {
         const Groups g = RB == 1 ? gr : regroup(gr, RB);
@@ -522,16 +522,18 @@ static bool launch_fmt(const uint16_t *X, const Groups &gr, int M, int K, int C,
     case 8: return launch_cfg<FMT, 8, 8, MR>(X, gr, M, K, C, s, fu);
     default: break;
     }
-    // sixteen waves (one activation row); the staged activations of a workgroup must fit in LDS.
-    // (The pair variant would exceed the registers a wave has at sixteen waves: longer rows are
-    // not paired.)
-    if constexpr (MR == 1) {
+    // sixteen waves (one activation row; two for 2-bit, whose activations need no bounce buffer);
+    // the staged activations of a workgroup must fit in LDS.  (The pair variant would exceed the
+    // registers a wave has at sixteen waves: longer rows are not paired.)
+    if constexpr (MR == 1 || (MR == 2 && FMT == TRI_FMT_2BIT)) {
         if (fu && fu->pair) return false;
         const int cst16 = (C + 63) / 64;
-        if (cst16 <= 6) return launch_cfg<FMT, 16, 6, 1>(X, gr, M, K, C, s, fu);
+        if (cst16 <= 6) return launch_cfg<FMT, 16, 6, MR>(X, gr, M, K, C, s, fu);
         if constexpr (FMT == TRI_FMT_2BIT) {
-            if (cst16 <= 8) return launch_cfg<FMT, 16, 8, 1>(X, gr, M, K, C, s, fu);
-            if (cst16 <= 12) return launch_cfg<FMT, 16, 12, 1>(X, gr, M, K, C, s, fu);
+            if (cst16 <= 8) return launch_cfg<FMT, 16, 8, MR>(X, gr, M, K, C, s, fu);
+            if constexpr (MR == 1) {
+                if (cst16 <= 12) return launch_cfg<FMT, 16, 12, 1>(X, gr, M, K, C, s, fu);
+            }
         }
     }
     return false;                                // longer rows: the streaming small-M kernel

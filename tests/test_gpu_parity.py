@@ -95,8 +95,9 @@ RAGGED = [(1, 1, 1), (1, 37, 1000), (1, 130, 4097), (1, 300, 81), (1, 33, 12000)
           (100, 11000, 1000), (300, 16001, 72),
           # long rows: 9..16 steps per wave of eight (2-bit and 1.6-bit), and past that the streaming kernel
           (5, 300, 24000), (16, 200, 30000), (8, 100, 40000), (12, 100, 40000), (20, 90, 26000),
-          # two activation rows on the M = 1 kernel's structure (eight and four waves, up to 8 steps)
-          (2, 300, 1000), (2, 4100, 4096), (2, 1000, 11008), (2, 90, 16384), (2, 50, 20000),
+          # two activation rows on the M = 1 kernel's structure (eight and four waves up to 8 steps;
+          # sixteen waves for longer 2-bit rows)
+          (2, 300, 1000), (2, 4100, 4096), (2, 1000, 11008), (2, 90, 16384), (2, 50, 20000), (2, 300, 30000),
           # wide matrices: the decode kernel with four 16-row blocks per workgroup (2-bit)
           (1, 13000, 1000), (2, 12900, 2048), (1, 14336, 4096),
           # three and four rows on the same structure (2-bit; 1.6-bit takes the batched kernel)
