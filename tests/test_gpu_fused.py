@@ -249,15 +249,16 @@ def test_block_step_fused(M):
     assert rel < 1e-2
 
 
+@pytest.mark.parametrize("M", [1, 2])
 @pytest.mark.parametrize("fmt", FMTS)
-def test_fused_residual_tall_matrix(fmt):
+def test_fused_residual_tall_matrix(fmt, M):
     """One tall matrix with a residual: the decode kernel's block loop adds the residual when it
     writes its outputs out (separate and in-place residual)."""
-    M, N, K = 1, 40007, 4096
+    N, K = 40007, 4096
     W, X, s = synth.layer_inputs(530 + fmt, 1, M, N, K)
     R = synth.activations(synth.rng_for(530 + fmt, 2, synth.STREAM_X), M, N)
     Wp = tri.pack(cuda(W), fmt)
-    say("fused residual tall N=%d fmt=%d" % (N, fmt))
+    say("fused residual tall M=%d N=%d fmt=%d" % (M, N, fmt))
     for inplace in (False, True):
         Y = run_fused(X, [Wp], [s], [N], K, fmt, Rs=[R], inplace=inplace)[0]
         check_layer_fused(Y, X, W, s, False, None, 1e-5, R, "tall residual fmt=%d inplace=%s" % (fmt, inplace))
