@@ -181,7 +181,8 @@ int tri_linear_fused(const _Float16 *X, const uint8_t *const *Wp, const float *s
 /* The algorithm tri_linear would pick for (M, N, K, fmt); TRI_EINVAL if invalid.  Up to
  * M = 16 it is TRI_ALGO_SMALLM; above, whichever of TRI_ALGO_SMALLM and TRI_ALGO_GEMM a cost
  * model fitted to MI355X timings says is faster (the small-M kernels' time grows with the
- * number of 16-row slices, the GEMM's with its rounds of 128 x 512 tiles). */
+ * number of 16-row slices; the GEMM's is flat while its 64 x 512 tiles fill at most half the
+ * CUs, then grows with its rounds of 128 x 512 tiles). */
 int tri_select_algo(int64_t M, int64_t N, int64_t K, int fmt);
 
 /* Human-readable name of a status code (static string, never NULL). */
