@@ -93,7 +93,10 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
     constexpr int PIECES = XH / 8;               // 16-byte activation pieces per chunk
     constexpr int NLD = (NCH * PIECES + 63) / 64;   // whole-line activation loads per lane
     static_assert(NCH <= 64, "chunks per wave");
-    __shared__ u32x4 xa[NW][NCH][MR][NOP];       // per wave: A operands of its chunks, per activation row
+    // per wave: A operands of its chunks, per activation row (four rows: one 16-byte pad per row,
+    // so the rows one read instruction touches fall in distinct banks)
+    constexpr int NOPP = MR == 4 ? NOP + 1 : NOP;
+    __shared__ u32x4 xa[NW][NCH][MR][NOPP];
     __shared__ u32x4 xraw[TWO ? 1 : NW][TWO ? 1 : NCH * PIECES];   // 1.6-bit: raw pieces
     // per wave and activation row: the 16 outputs of each block, sum x (, sum x^2)
     __shared__ float red[PS ? 2 : 1][NW][MR][16 * RB + (NORM ? 2 : 1)];   // (block loop: two, alternating)
@@ -407,34 +410,45 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
     }
 }
 
+// One matrix of many blocks (at least kLoopBlocksPerSlot per resident workgroup): a resident
+// grid that loops over the blocks.  Eight waves at most (sixteen would spill the second register
+// set); no glue but the residual.
+template <int FMT, int NW, int CST, int MR>
+static bool launch_loop(const uint16_t *X, const Groups &gr, int M, int K, int C, hipStream_t s, const Fusion &f)
+{
+    constexpr int kXaBytes = NW * 4 * CST * MR * ((FMT == TRI_FMT_2BIT ? 8 : 10) + (MR == 4 ? 1 : 0)) * 16;
+    if constexpr (NW > 8 || (MR > 1 && kXaBytes > 100 * 1024)) {   // (the staged operands' LDS, as below)
+        return false;
+    } else {
+        if (gr.G != 1 || (int64_t)gr.N[0] * C * 16 >= ((int64_t)1 << 31)) return false;
+        static const int resident = [] {
+            int n = 0;
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_mv1<FMT, NW, CST, 0, true, MR, 1, true>, 64 * NW, 0) !=
+                    hipSuccess ||
+                n < 1)
+                n = 1;
+            return n * kCUs;
+        }();
+        if ((int64_t)gr.blk[1] < (int64_t)kLoopBlocksPerSlot * resident) return false;
+        hipLaunchKernelGGL((k_mv1<FMT, NW, CST, 0, true, MR, 1, true>), dim3(resident), dim3(64 * NW), 0, s, X, gr, M, K,
+                           C, f);
+        return true;
+    }
+}
+
 template <int FMT, int NW, int CST, int GL, int MR, int RB>
 static bool launch_gl(const uint16_t *X, const Groups &gr, int M, int K, int C, hipStream_t s, const Fusion &f)
 {
     // several activation rows: only while the staged A operands of the workgroup stay below
     // 100 KB of LDS (136 KB at sixteen waves, whose registers hold one workgroup per CU anyway)
-    constexpr int kXaBytes = NW * 4 * CST * MR * (FMT == TRI_FMT_2BIT ? 8 : 10) * 16;
+    constexpr int kXaBytes = NW * 4 * CST * MR * ((FMT == TRI_FMT_2BIT ? 8 : 10) + (MR == 4 ? 1 : 0)) * 16;
     if constexpr (MR > 1 && kXaBytes > (NW == 16 ? 136 : 100) * 1024) {
         return false;
     } else {
         const Groups g = RB == 1 ? gr : regroup(gr, RB);
         const dim3 grid(g.blk[g.G]), block(64 * NW);
-        if constexpr (GL == 0 && RB == 1 && NW <= 8) {
-            // one matrix of many blocks: a resident grid that loops over the blocks (sixteen waves
-            // would spill the second register set)
-            if (g.G == 1 && (int64_t)gr.N[0] * C * 16 < ((int64_t)1 << 31)) {
-                static const int resident = [] {
-                    int n = 0;
-                    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_mv1<FMT, NW, CST, 0, true, MR, 1, true>,
-                                                                     64 * NW, 0) != hipSuccess || n < 1)
-                        n = 1;
-                    return n * kCUs;
-                }();
-                if ((int64_t)g.blk[1] >= (int64_t)kLoopBlocksPerSlot * resident) {
-                    hipLaunchKernelGGL((k_mv1<FMT, NW, CST, 0, true, MR, 1, true>), dim3(resident), block, 0, s, X, g,
-                                       M, K, C, f);
-                    return true;
-                }
-            }
+        if constexpr (GL == 0 && RB == 1) {
+            if (launch_loop<FMT, NW, CST, MR>(X, gr, M, K, C, s, f)) return true;
         }
         if (g.G == 1)
             hipLaunchKernelGGL((k_mv1<FMT, NW, CST, GL, true, MR, RB, false>), grid, block, 0, s, X, g, M, K, C, f);
@@ -471,7 +485,10 @@ static bool launch_cfg(const uint16_t *X, const Groups &gr, int M, int K, int C,
     const bool rb4 = wide_rb<FMT, NW, CST, MR>(gr, fu);
     if constexpr (MR > 1) {                      // (no glue but the residual)
         if constexpr (FMT == TRI_FMT_2BIT && NW == 8 && (MR == 4 || CST <= 6)) {
-            if (rb4) return launch_gl<FMT, NW, CST, 0, MR, 4>(X, gr, M, K, C, s, f);
+            // (a tall matrix: the block loop before four-block workgroups)
+            if (rb4 && !launch_loop<FMT, NW, CST, MR>(X, gr, M, K, C, s, f))
+                return launch_gl<FMT, NW, CST, 0, MR, 4>(X, gr, M, K, C, s, f);
+            if (rb4) return true;
         }
         return launch_gl<FMT, NW, CST, 0, MR, 1>(X, gr, M, K, C, s, f);
     } else {

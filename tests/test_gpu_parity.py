@@ -410,7 +410,7 @@ def test_grouped_large_grid_same_as_single(fmt, M):
 TALL = [(tri.TRI_FMT_2BIT, 1, 40007, 4096), (tri.TRI_FMT_2BIT, 2, 40007, 4096),
         (tri.TRI_FMT_2BIT, 1, 30011, 8192), (tri.TRI_FMT_1P6BIT, 1, 40003, 4096),
         (tri.TRI_FMT_1P6BIT, 2, 40003, 8192), (tri.TRI_FMT_2BIT, 1, 212005, 512),
-        (tri.TRI_FMT_2BIT, 2, 212005, 512)]
+        (tri.TRI_FMT_2BIT, 2, 212005, 512), (tri.TRI_FMT_2BIT, 3, 30011, 8192), (tri.TRI_FMT_2BIT, 4, 40007, 4096)]
 
 
 @pytest.mark.parametrize("fmt,M,N,K", TALL)
