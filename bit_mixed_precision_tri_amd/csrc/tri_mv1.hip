@@ -417,7 +417,7 @@ template <int FMT, int NW, int CST, int MR>
 static bool launch_loop(const uint16_t *X, const Groups &gr, int M, int K, int C, hipStream_t s, const Fusion &f)
 {
     constexpr int kXaBytes = NW * 4 * CST * MR * ((FMT == TRI_FMT_2BIT ? 8 : 10) + (MR == 4 ? 1 : 0)) * 16;
-    if constexpr (NW > 8 || (MR > 1 && kXaBytes > 100 * 1024)) {   // (the staged operands' LDS, as below)
+    if constexpr (NW > 8 || (MR > 1 && kXaBytes > (MR == 4 ? 120 : 100) * 1024)) {   // (the staged operands' LDS, as below)
         return false;
     } else {
         if (gr.G != 1 || (int64_t)gr.N[0] * C * 16 >= ((int64_t)1 << 31)) return false;
@@ -440,9 +440,10 @@ template <int FMT, int NW, int CST, int GL, int MR, int RB>
 static bool launch_gl(const uint16_t *X, const Groups &gr, int M, int K, int C, hipStream_t s, const Fusion &f)
 {
     // several activation rows: only while the staged A operands of the workgroup stay below
-    // 100 KB of LDS (136 KB at sixteen waves, whose registers hold one workgroup per CU anyway)
+    // 100 KB of LDS (120 KB at four rows, 136 KB at sixteen waves, whose registers hold one
+    // workgroup per CU anyway)
     constexpr int kXaBytes = NW * 4 * CST * MR * ((FMT == TRI_FMT_2BIT ? 8 : 10) + (MR == 4 ? 1 : 0)) * 16;
-    if constexpr (MR > 1 && kXaBytes > (NW == 16 ? 136 : 100) * 1024) {
+    if constexpr (MR > 1 && kXaBytes > (NW == 16 ? 136 : MR == 4 ? 120 : 100) * 1024) {
         return false;
     } else {
         const Groups g = RB == 1 ? gr : regroup(gr, RB);
