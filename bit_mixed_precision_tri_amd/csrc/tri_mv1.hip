@@ -451,6 +451,7 @@ static bool launch_gl(const uint16_t *X, const Groups &gr, int M, int K, int C, 
         if constexpr (GL == 0 && RB == 1) {
             if (launch_loop<FMT, NW, CST, MR>(X, gr, M, K, C, s, f)) return true;
         }
+        if constexpr (FMT == TRI_FMT_1P6BIT && MR == 4) return false;   // (1.6-bit, four rows: the block loop only)
         if (g.G == 1)
             hipLaunchKernelGGL((k_mv1<FMT, NW, CST, GL, true, MR, RB, false>), grid, block, 0, s, X, g, M, K, C, f);
         else
@@ -578,8 +579,11 @@ bool launch_mvr(const uint16_t *X, const Groups &gr, int M, int K, int fmt, hipS
     if (fmt == TRI_FMT_2BIT)
         return M == 2 ? launch_fmt<TRI_FMT_2BIT, 2>(X, gr, M, K, C, s, fu)
                       : launch_fmt<TRI_FMT_2BIT, 4>(X, gr, M, K, C, s, fu);
-    // 1.6-bit: two rows only (four measured 10-50% slower than the batched kernel)
-    return M == 2 && launch_fmt<TRI_FMT_1P6BIT, 2>(X, gr, M, K, C, s, fu);
+    // 1.6-bit: two rows; three and four only as the block loop over a tall matrix (8192 -> 28672
+    // at M = 4: 32.4 -> 22.5 us; a one-shot grid of four rows was 3-50% slower than the batched
+    // kernel)
+    return M == 2 ? launch_fmt<TRI_FMT_1P6BIT, 2>(X, gr, M, K, C, s, fu)
+                  : launch_fmt<TRI_FMT_1P6BIT, 4>(X, gr, M, K, C, s, fu);
 }
 
 }  // namespace tri
