@@ -42,17 +42,18 @@ int check_linear(const void *X, const void *Wp, int64_t M, int64_t N, int64_t K,
 int select_algo(int64_t M, int64_t N, int64_t K, int fmt)
 {
     if (M <= 16) return TRI_ALGO_SMALLM;
+    const int64_t cus = cu_count();
     const bool two = fmt == TRI_FMT_2BIT;
     double c = two ? 0.10 : 0.127;               // ps
     if (K > (two ? 32768 : 35840)) c *= two ? 5.0 : 1.9;
     else if (K > (two ? 16384 : 20480)) c *= two ? 1.6 : 1.2;
     const int64_t tn = (N + 511) / 512;
     const int64_t T64 = ((M + 63) / 64) * tn, T = ((M + 127) / 128) * tn;
-    const int64_t r = T % kCUs;
-    const int64_t R = (r > 0 && r <= kCUs / 2) ? 2 * (T / kCUs) + 1 : 2 * ((T + kCUs - 1) / kCUs);
+    const int64_t r = T % cus;
+    const int64_t R = (r > 0 && r <= cus / 2) ? 2 * (T / cus) + 1 : 2 * ((T + cus - 1) / cus);
     const double small = (double)((M + 15) / 16) * (double)N * c;
-    const double gemm = T64 <= kCUs / 4 ? (two ? 4800.0 : 6300.0)
-                      : T64 <= kCUs / 2 ? (two ? 8800.0 : 10700.0)
+    const double gemm = T64 <= cus / 4 ? (two ? 4800.0 : 6300.0)
+                      : T64 <= cus / 2 ? (two ? 8800.0 : 10700.0)
                                         : (two ? 13000.0 : 16000.0) * (double)R;
     return small < gemm ? TRI_ALGO_SMALLM : TRI_ALGO_GEMM;
 }
@@ -91,6 +92,21 @@ int run_linear(const _Float16 *X, const uint8_t *Wp, float scale, int64_t M, int
 }
 
 }  // namespace
+
+int tri::cu_count()
+{
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (dev >= 0 && dev < kMaxDevices) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) return 256;
+    if (dev >= 0 && dev < kMaxDevices) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
 
 extern "C" {
 

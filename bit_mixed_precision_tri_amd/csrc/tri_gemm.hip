@@ -357,17 +357,18 @@ static int launch_fmt(const uint16_t *X, const uint8_t *Wp, float scale, int M, 
     // half-empty 128-row tiles, and twice the workgroups of 128-row quarter tiles (30-40% faster
     // where there are at most 64 such tiles; up to 128, two workgroups share a CU and still win
     // a few per cent)
+    const int cus = cu_count();
     const int tiles_m64 = (M + 63) / 64;
     const int64_t T64 = (int64_t)tiles_m64 * tiles_n;
-    if (T64 <= kCUs / 2) {
+    if (T64 <= cus / 2) {
         hipLaunchKernelGGL((k_gemm<FMT, 1, 64>), dim3((unsigned)(4 * T64)), dim3(256), 0, s, X, Wp, scale, M, N, K, C,
                            tiles_m64, tiles_n, 0, Y);
         return hipGetLastError() == hipSuccess ? TRI_OK : TRI_EHIP;
     }
     // A last round of full tiles that would leave more than half of the CUs idle is run as
     // twice as many half-width tiles instead, by a second launch.
-    const int r = (int)(T % kCUs);
-    const int tail = (r > 0 && r <= kCUs / 2) ? r : 0;
+    const int r = (int)(T % cus);
+    const int tail = (r > 0 && r <= cus / 2) ? r : 0;
     const int full = (int)T - tail;
     if (full > 0)
         hipLaunchKernelGGL((k_gemm<FMT, 4, 128>), dim3((unsigned)full), dim3(256), 0, s, X, Wp, scale, M, N, K, C, tiles_m,

@@ -1,12 +1,40 @@
 // tri_internal.h -- host-side declarations shared by the libtri translation units.
 #pragma once
 #include <stdint.h>
+#include <atomic>
 #include <hip/hip_runtime.h>
 #include "../../include/tri.h"
 
 namespace tri {
 
-constexpr int kCUs = 256;                        // compute units of an MI355X
+// What the library caches: per device (by its ordinal, up to kMaxDevices), the device's compute
+// unit count and, per block-loop kernel variant, how many of its workgroups one CU holds.  Each
+// entry is written once, by the first call that needs it on that device, with the value the HIP
+// runtime reports; nothing else outlives a call.
+constexpr int kMaxDevices = 64;
+
+// Compute units of the calling thread's current device (256 on an MI355X).  Where no device can
+// be queried (a host without a GPU, where only the host-side kernel choice runs) the MI355X
+// figure is taken.
+int cu_count();
+
+// Workgroups of KERNEL, launched with `threads` threads, that one CU of the current device holds
+// at once (at least 1).
+template <auto KERNEL>
+int resident_per_cu(int threads)
+{
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+    if (dev >= 0 && dev < kMaxDevices) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, KERNEL, threads, 0) != hipSuccess || n < 1) n = 1;
+    if (dev >= 0 && dev < kMaxDevices) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
 
 inline int64_t row_bytes(int64_t K, int fmt)
 {
@@ -69,7 +97,7 @@ inline int choose_rb(const Groups &gr, int M)
 {
     const int64_t slices = (M + 15) / 16;
     for (int rb = 4; rb > 1; rb /= 2)
-        if (regroup(gr, rb).blk[gr.G] * slices >= kCUs * 5 / 8) return rb;
+        if (regroup(gr, rb).blk[gr.G] * slices >= cu_count() * 5 / 8) return rb;
     return 1;
 }
 

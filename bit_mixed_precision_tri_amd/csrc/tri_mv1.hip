@@ -421,14 +421,7 @@ static bool launch_loop(const uint16_t *X, const Groups &gr, int M, int K, int C
         return false;
     } else {
         if (gr.G != 1 || (int64_t)gr.N[0] * C * 16 >= ((int64_t)1 << 31)) return false;
-        static const int resident = [] {
-            int n = 0;
-            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_mv1<FMT, NW, CST, 0, true, MR, 1, true>, 64 * NW, 0) !=
-                    hipSuccess ||
-                n < 1)
-                n = 1;
-            return n * kCUs;
-        }();
+        const int resident = resident_per_cu<k_mv1<FMT, NW, CST, 0, true, MR, 1, true>>(64 * NW) * cu_count();
         if ((int64_t)gr.blk[1] < (int64_t)kLoopBlocksPerSlot * resident) return false;
         hipLaunchKernelGGL((k_mv1<FMT, NW, CST, 0, true, MR, 1, true>), dim3(resident), dim3(64 * NW), 0, s, X, gr, M, K,
                            C, f);
@@ -476,7 +469,7 @@ static bool wide_rb(const Groups &gr, const Fusion *fu)
         const int w = regroup(gr, 4).blk[gr.G];
         if (glue_bits(fu)) return false;
         if constexpr (MR == 4) return w >= 160;
-        else return w >= (MR == 1 ? 200 : 160) && w <= kCUs;
+        else return w >= (MR == 1 ? 200 : 160) && w <= cu_count();
     }
 }
 

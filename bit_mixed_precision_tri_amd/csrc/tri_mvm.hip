@@ -395,7 +395,7 @@ static bool launch_mt(const uint16_t *X, const Groups &gr, int M, int K, int C, 
     // workgroup), four-wave workgroups (half the LDS) let two share a CU (measured 20% faster at
     // 4096 -> 11008 with one block per workgroup; slower where the grid fits)
     if constexpr (FMT == TRI_FMT_1P6BIT && MT == 16) {
-        if (!glue_bits(fu) && rb == 1 && (int64_t)gr.blk[gr.G] * ((M + 15) / 16) > kCUs) {
+        if (!glue_bits(fu) && rb == 1 && (int64_t)gr.blk[gr.G] * ((M + 15) / 16) > cu_count()) {
             switch ((C + 15) / 16) {
             case 1: return launch_cfg<FMT, MT, 4, 1>(X, gr, M, K, C, s, fu);
             case 2: return launch_cfg<FMT, MT, 4, 2>(X, gr, M, K, C, s, fu);

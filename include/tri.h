@@ -22,8 +22,10 @@
  *
  * Conventions for every call:
  *  - All array pointers are DEVICE pointers owned by the caller.  The library
- *    allocates no memory and keeps no mutable global state; calls are
- *    thread-safe and deterministic (no atomics; the reduction order is fixed).
+ *    allocates no memory.  The only state it keeps is, per device, the compute
+ *    unit count and the resident workgroups of a few kernel variants, each
+ *    queried from the HIP runtime once and never changed; calls are thread-safe
+ *    and deterministic (no atomics; the reduction order is fixed).
  *  - Work is enqueued asynchronously on `stream` (0 = the null stream).  A
  *    device fault surfaces at the caller's next synchronisation.
  *  - Argument checks run on the host before anything is launched; on failure
@@ -61,8 +63,15 @@ enum {
                               trits decoded in registers (prefill) */
 };
 
-/* Bytes of one packed row: 16*ceil(K/64) (2-bit) or 16*ceil(K/80) (1.6-bit).
- * Returns -1 if K < 1 or fmt is unknown. */
+/* Bytes of one packed row of K trits: 16*ceil(K/64) (2-bit) or 16*ceil(K/80)
+ * (1.6-bit).  The densities are the pages' (Pith review, "Core claim": base-4 and
+ * base-3 encodings; "What carries the argument": 5 trits in 8 bits since
+ * 3^5 < 2^8); the row padding is this library's reading of a layout the pages
+ * leave open: every row is padded with zero trits to whole 16-byte chunks (64
+ * trits in 2-bit, 80 in 1.6-bit), so a row starts 16-byte aligned and is read
+ * with 16-byte loads.  At K a multiple of 64 the 2-bit row is exactly K/4 bytes;
+ * a 1.6-bit row exceeds ceil(K/5) by at most 15 bytes.
+ * Returns -1 if K < 1 or fmt is unknown; pure host arithmetic, launches nothing. */
 int64_t tri_row_bytes(int64_t K, int fmt);
 
 /* 2-bit packing (Pith review, "Core claim": base-4 encoding).
