@@ -6,8 +6,8 @@ three projections of a LLaMA-style block at hidden 4096 / MLP 11008
 (4096x4096, 4096->11008, 11008->4096).  One step = the three tri_linear launches
 on cold weights: every matrix rotates over 64 distinct copies (1.7 GB in all),
 so the 256 MB Infinity Cache cannot serve a step's weights.  The value is
-effective HBM bandwidth: (packed weights as stored + fp16 X read + fp16 Y
-written) per step / wall time per step, inputs resident in HBM.
+effective HBM bandwidth: (packed weights as stored + fp16 X read) per step /
+wall time per step, inputs resident in HBM.
 
 Timing.  The timed region replays a HIP graph of the steps (captured once from
 the same tri_linear calls), so the host's per-launch cost stays out of it.
@@ -45,8 +45,23 @@ def log(*a):
 
 
 def effective_bytes(M, N, K, fmt):
+    """Effective bytes of one layer launch: the packed weights as stored plus the fp16 activations
+    read (the output's 2*M*N bytes are not counted)."""
     import bit_mixed_precision_tri_amd as tri
-    return N * tri.tri_row_bytes(K, fmt) + 2 * M * K + 2 * M * N
+    return N * tri.tri_row_bytes(K, fmt) + 2 * M * K
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo) and its logical CPU count."""
+    name = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                name = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return name, os.cpu_count()
 
 
 class Layer:
@@ -173,7 +188,9 @@ def cpu_baseline(shapes, budget_s=10.0):
         if len(times) >= 200:
             break
     t = float(np.median(times))
+    model, ncpu = cpu_model()
     return {"value": round(total_bytes / t / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "cpu_model": model, "host_logical_cpus": ncpu,
             "sample": "the full decode step (3 shapes, M=1, 2-bit: unpack + float64 layer) run %d times in ~%d s, "
                       "median %.3f s per step" % (len(times), budget_s, t)}
 
@@ -236,7 +253,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--skip-extra", action="store_true", help="skip the batched, block and prefill workloads")
     ap.add_argument("--skip-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--profile", choices=["decode", "copy", "prefill"],
+    ap.add_argument("--floor", action="store_true",
+                    help="only the decode floor: empty and loads-only probes on the decode grid, streaming reads")
+    ap.add_argument("--profile", choices=["decode", "copy", "prefill", "batched", "floor"],
                     help="only launch one workload a few times (for rocprofv3 --pmc runs)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -258,6 +277,9 @@ def main():
 
     if args.profile:
         return profile_mode(args.profile)
+    if args.floor:
+        print(json.dumps({"floor": bench_floor(Clock())}), flush=True)
+        return
 
     # ---- headline: decode GEMV, M = 1, 2-bit, three shapes, cold weights
     dcfg = configs.DECODE
@@ -306,6 +328,7 @@ def main():
         floors.append({"shape": name, "bytes": nb, "read_us": round(t * 1e6, 3), "GBps": round(nb / t / 1e9, 1)})
     for so, fl in zip(shapes_out, floors):      # the read floor's time over the kernel's: 1.0 = at the floor
         so["read_floor_over_kernel"] = round(fl["read_us"] / so["kernel_us"], 3)
+    small = bench_small(clock)
     ctr = counters()
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -329,6 +352,7 @@ def main():
                    "TFLOP/s to compare with (vs_baseline is null)",
         "per_shape": shapes_out,
         "read_floor": floors,
+        "small": small,
     }
     if not args.skip_extra:
         out["decode_1p6bit"] = bench_decode_1p6(clock)
@@ -342,6 +366,26 @@ def main():
         out["cpu_baseline"] = cpu_baseline(dcfg["shapes"])
         out["cpu_oracle_detail"] = cpu_oracle_detail(dcfg["shapes"])
     print(json.dumps(out), flush=True)
+
+
+def bench_small(clock):
+    """The small layer (M = 1, K = 512, N = 256, scale 0.02) in both formats: latency per launch
+    (32 KB of 2-bit weights are far below any bandwidth regime), timed as 200 back-to-back launches
+    with events around a sleep-held queue and as a replayed HIP graph of them."""
+    import torch
+    from bit_mixed_precision_tri_amd import configs
+    cfg = configs.SMALL
+    res = []
+    for fmt in cfg["fmts"]:
+        L = Layer(cfg["workload_id"], 0, cfg["M"], cfg["N"], cfg["K"], fmt, cfg["scale"])
+        t_ev, _ = clock.run([L.launch] * 200)
+        t_gr = graph_time(L.launch, 200, replays=3)
+        res.append({"M": cfg["M"], "K": cfg["K"], "N": cfg["N"], "format": configs.FMT_NAMES[fmt],
+                    "bytes": L.bytes, "kernel_us_events": round(t_ev * 1e6, 3),
+                    "kernel_us_graph": round(t_gr * 1e6, 3)})
+        del L
+        torch.cuda.empty_cache()
+    return res
 
 
 def bench_batched(clock):
@@ -600,6 +644,85 @@ def bench_quantize(clock):
     return res
 
 
+def bench_floor(clock):
+    """Where a decode launch's time goes (M = 1, 2-bit, the three decode shapes, cold weights):
+    the decode kernel against (a) an empty kernel on the decode kernel's grid (the fixed cost of a
+    launch of that many workgroups), (b) the decode kernel's loads alone on the same grid
+    (tri_probe_rows: the same weight chunks per lane and the same activation loads, no decode,
+    contraction, reduction or epilogue), (c) streaming reads of the same bytes: the one-load-per-
+    thread grid (tri_probe_read) and resident grids of 256..2048 workgroups keeping 1..8 loads in
+    flight per lane (tri_probe_stream; the best of them is the read floor).  Every figure is the
+    mean per launch of 200 back-to-back launches, timed two ways: HIP events around a sleep-held
+    queue (launch gaps of an in-order stream included) and a replayed HIP graph of the 200."""
+    import torch
+    import bit_mixed_precision_tri_amd as tri
+    from bit_mixed_precision_tri_amd import configs
+    F2 = tri.TRI_FMT_2BIT
+    cfg = configs.DECODE
+    reps = 200
+
+    def both(calls):
+        t_ev, _ = clock.run(calls)
+        k = [0]
+
+        def step():
+            calls[k[0] % len(calls)]()
+            k[0] += 1
+        t_gr = graph_time(step, len(calls), replays=3)
+        return round(t_ev * 1e6, 3), round(t_gr * 1e6, 3)
+
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    out = []
+    for li, (name, K, N) in enumerate(cfg["shapes"]):
+        L = Layer(cfg["workload_id"], li, 1, N, K, F2)
+        wg = (N + 15) // 16
+        nb = N * tri.tri_row_bytes(K, F2)
+        Yp = torch.empty(N, dtype=torch.float16, device="cuda")
+        rec = {"shape": name, "K": K, "N": N, "weight_bytes": nb, "workgroups": wg, "threads": 512}
+        rec["decode_us"] = both([L.launch] * reps)
+        rec["empty_same_grid_us"] = both([lambda: tri.tri_probe_empty(wg, 512, sink)] * reps)
+        rec["empty_one_wave_us"] = both([lambda: tri.tri_probe_empty(1, 64, sink)] * reps)
+        ctr = [0]
+
+        def rows():
+            Wp = L.pool[ctr[0] % L.pool.shape[0]]
+            ctr[0] += 1
+            tri.tri_probe_rows(L.X, Wp, N, K, F2, 8, Yp)
+        rec["loads_only_us"] = both([rows] * reps)
+        del L
+        torch.cuda.empty_cache()
+        ncopies = max(1, -(-(1 << 30) // nb))
+        pool = torch.empty((ncopies, nb), dtype=torch.uint8, device="cuda")
+        pool.fill_(1)
+        c2 = [0]
+
+        def rd():
+            tri.tri_probe_read(pool[c2[0] % ncopies], nb, sink)
+            c2[0] += 1
+        rec["read_grid_stride_us"] = both([rd] * reps)
+        best = None
+        sweep = []
+        for wgs in (256, 512, 1024, 2048):
+            for u in (1, 2, 4, 8):
+                if wgs * 256 * u * 16 > 4 * nb:
+                    continue
+
+                def st(wgs=wgs, u=u):
+                    tri.tri_probe_stream(pool[c2[0] % ncopies], nb, wgs, u, sink)
+                    c2[0] += 1
+                t = both([st] * reps)
+                sweep.append({"workgroups": wgs, "unroll": u, "us": t})
+                if best is None or t[0] < best["us"][0]:
+                    best = sweep[-1]
+        rec["stream_sweep"] = sweep
+        rec["stream_best"] = best
+        del pool
+        torch.cuda.empty_cache()
+        out.append(rec)
+        log("floor", json.dumps(rec))
+    return out
+
+
 def profile_mode(which):
     """Launch one workload a few times and exit (for rocprofv3 counter passes)."""
     import torch
@@ -622,6 +745,19 @@ def profile_mode(which):
             torch.cuda.synchronize()
             del L
             torch.cuda.empty_cache()
+    elif which == "batched":
+        cfg = configs.BATCHED
+        for fmt in cfg["fmts"]:
+            for li, (name, K, N) in enumerate(cfg["shapes"]):
+                for M in (8, 16):
+                    L = Layer(cfg["workload_id"], 10 * li + M, M, N, K, fmt, copies=8)
+                    for _ in range(10):
+                        L.launch()
+                    torch.cuda.synchronize()
+                    del L
+                    torch.cuda.empty_cache()
+    elif which == "floor":
+        bench_floor(Clock())
     elif which == "copy":
         nb = 64 << 20
         src = torch.ones(nb, dtype=torch.uint8, device="cuda")

@@ -70,6 +70,12 @@ def lib():
         L.tri_probe_read.restype = i32
         L.tri_probe_copy.argtypes = [p, p, i64, p]
         L.tri_probe_copy.restype = i32
+        L.tri_probe_empty.argtypes = [i64, i32, p, p]
+        L.tri_probe_empty.restype = i32
+        L.tri_probe_rows.argtypes = [p, p, i64, i64, i32, i32, p, p]
+        L.tri_probe_rows.restype = i32
+        L.tri_probe_stream.argtypes = [p, i64, i32, i32, p, p]
+        L.tri_probe_stream.restype = i32
         _lib = L
     return _lib
 
@@ -183,6 +189,20 @@ def tri_probe_read(src, nbytes, sink, stream=None):
 
 def tri_probe_copy(src, dst, nbytes, stream=None):
     return _check(lib().tri_probe_copy(_ptr(src), _ptr(dst), int(nbytes), _stream(stream)), "tri_probe_copy")
+
+
+def tri_probe_empty(workgroups, threads, sink, stream=None):
+    return _check(lib().tri_probe_empty(int(workgroups), int(threads), _ptr(sink), _stream(stream)), "tri_probe_empty")
+
+
+def tri_probe_rows(X, Wp, N, K, fmt, waves, Y, stream=None):
+    return _check(lib().tri_probe_rows(_ptr(X), _ptr(Wp), int(N), int(K), int(fmt), int(waves), _ptr(Y),
+                                       _stream(stream)), "tri_probe_rows")
+
+
+def tri_probe_stream(src, nbytes, workgroups, unroll, sink, stream=None):
+    return _check(lib().tri_probe_stream(_ptr(src), int(nbytes), int(workgroups), int(unroll), _ptr(sink),
+                                         _stream(stream)), "tri_probe_stream")
 
 
 # ---------------------------------------------------------------- allocating helpers

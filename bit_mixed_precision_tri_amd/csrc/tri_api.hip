@@ -275,4 +275,31 @@ int tri_probe_copy(const void *src, void *dst, int64_t bytes, hipStream_t stream
     return launch_probe_copy(src, dst, bytes, stream);
 }
 
+int tri_probe_empty(int64_t workgroups, int threads, uint32_t *sink, hipStream_t stream)
+{
+    if (!sink || workgroups < 1 || workgroups >= kMaxDim || threads < 64 || threads > 1024 || (threads % 64) != 0)
+        return TRI_EINVAL;
+    return launch_probe_empty(workgroups, threads, sink, stream);
+}
+
+int tri_probe_rows(const _Float16 *X, const uint8_t *Wp, int64_t N, int64_t K, int fmt, int waves, _Float16 *Y,
+                   hipStream_t stream)
+{
+    if (!X || !Wp || !Y || N < 1 || K < 1 || N >= kMaxDim || K >= kMaxDim || !known_fmt(fmt)) return TRI_EINVAL;
+    if (waves != 4 && waves != 8) return TRI_EINVAL;
+    if ((row_bytes(K, fmt) / 16 + 4 * waves - 1) / (4 * waves) > 8 || N * row_bytes(K, fmt) >= kMaxDim)
+        return TRI_EINVAL;
+    if (misaligned(X) || misaligned(Wp)) return TRI_EALIGN;
+    return launch_probe_rows(reinterpret_cast<const uint16_t *>(X), Wp, (int)N, (int)K, fmt, waves,
+                             reinterpret_cast<uint16_t *>(Y), stream);
+}
+
+int tri_probe_stream(const void *src, int64_t bytes, int workgroups, int unroll, uint32_t *sink, hipStream_t stream)
+{
+    if (!src || !sink || bytes < 16 || (bytes % 16) != 0 || bytes >= kMaxDim || workgroups < 1) return TRI_EINVAL;
+    if (unroll != 1 && unroll != 2 && unroll != 4 && unroll != 8) return TRI_EINVAL;
+    if (misaligned(src)) return TRI_EALIGN;
+    return launch_probe_stream(src, bytes, workgroups, unroll, sink, stream);
+}
+
 }  // extern "C"

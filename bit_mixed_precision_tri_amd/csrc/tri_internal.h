@@ -165,5 +165,9 @@ int launch_gemm(const uint16_t *X, const uint8_t *Wp, float scale, int64_t M, in
                 hipStream_t s);
 int launch_probe_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t s);
 int launch_probe_copy(const void *src, void *dst, int64_t bytes, hipStream_t s);
+int launch_probe_empty(int64_t workgroups, int threads, uint32_t *sink, hipStream_t s);
+int launch_probe_rows(const uint16_t *X, const uint8_t *Wp, int N, int K, int fmt, int waves, uint16_t *Y,
+                      hipStream_t s);
+int launch_probe_stream(const void *src, int64_t bytes, int workgroups, int unroll, uint32_t *sink, hipStream_t s);
 
 }  // namespace tri

@@ -207,6 +207,25 @@ const char *tri_status_string(int code);
 int tri_probe_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t stream);
 int tri_probe_copy(const void *src, void *dst, int64_t bytes, hipStream_t stream);
 
+/* Launch-cost and read-pattern probes of the decode floor (measurement aids).
+ * tri_probe_empty launches an empty kernel of `workgroups` workgroups of
+ * `threads` threads (64..1024, a multiple of 64); sink (4 bytes) is never written.
+ * tri_probe_rows issues exactly the loads of the one-row decode kernel over an N x
+ * tri_row_bytes(K, fmt) packed matrix and a K-wide fp16 row X (16 rows per
+ * workgroup of `waves` = 4 or 8 waves, the same chunk of every lane and the same
+ * whole-line activation loads) and nothing else: it writes one 16-bit word per
+ * matrix row to Y (N fp16 slots) that folds the bytes it read; rows longer than 8
+ * steps of 4 chunks per wave give TRI_EINVAL.  tri_probe_stream reads `bytes`
+ * bytes (a multiple of 16, below 2^31) with a grid of `workgroups` workgroups of
+ * 256 threads, each lane keeping `unroll` (1, 2, 4 or 8) 16-byte loads in flight
+ * per round; sink is written only if a data-dependent test that practically never
+ * holds passes.  Errors: TRI_EINVAL, TRI_EALIGN (X, Wp, src), TRI_EHIP. */
+int tri_probe_empty(int64_t workgroups, int threads, uint32_t *sink, hipStream_t stream);
+int tri_probe_rows(const _Float16 *X, const uint8_t *Wp, int64_t N, int64_t K, int fmt, int waves,
+                   _Float16 *Y, hipStream_t stream);
+int tri_probe_stream(const void *src, int64_t bytes, int workgroups, int unroll, uint32_t *sink,
+                     hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
