@@ -54,6 +54,8 @@ def lib():
         L.tri_quantize_workspace_bytes.restype = i64
         L.tri_quantize.argtypes = [p, i64, i64, i32, p, p, p, i64, p]
         L.tri_quantize.restype = i32
+        L.tri_quantize_noalloc.argtypes = [p, i64, i64, i32, p, p, p]
+        L.tri_quantize_noalloc.restype = i32
         L.tri_linear.argtypes = [p, p, ctypes.c_float, i64, i64, i64, i32, p, p]
         L.tri_linear.restype = i32
         L.tri_linear_algo.argtypes = [p, p, ctypes.c_float, i64, i64, i64, i32, p, i32, p]
@@ -128,6 +130,11 @@ def tri_quantize(W, N, K, fmt, Wp, scale_out, workspace, workspace_bytes, stream
                                      int(workspace_bytes), _stream(stream)), "tri_quantize")
 
 
+def tri_quantize_noalloc(W, N, K, fmt, Wp, scale_out, stream=None):
+    return _check(lib().tri_quantize_noalloc(_ptr(W), int(N), int(K), int(fmt), _ptr(Wp), _ptr(scale_out),
+                                             _stream(stream)), "tri_quantize_noalloc")
+
+
 def tri_linear(X, Wp, scale, M, N, K, fmt, Y, stream=None):
     return _check(lib().tri_linear(_ptr(X), _ptr(Wp), float(scale), int(M), int(N), int(K), int(fmt), _ptr(Y),
                                    _stream(stream)), "tri_linear")
@@ -139,6 +146,7 @@ def tri_linear_algo(X, Wp, scale, M, N, K, fmt, Y, algo, stream=None):
 
 
 TRI_MAX_GROUPS = 4
+TRI_QUANTIZE_SCRATCH_BYTES = 16384
 
 
 def tri_linear_grouped(X, Wps, scales, M, Ns, K, fmt, Ys, stream=None):

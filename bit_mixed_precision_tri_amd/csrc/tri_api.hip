@@ -129,6 +129,18 @@ int tri_quantize(const float *W, int64_t N, int64_t K, int fmt, uint8_t *Wp, flo
     return launch_quantize(W, N, K, fmt, Wp, scale_out, workspace, stream);
 }
 
+int tri_quantize_noalloc(const float *W, int64_t N, int64_t K, int fmt, uint8_t *Wp, float *scale_out,
+                         hipStream_t stream)
+{
+    if (!W || !Wp || !scale_out || !known_fmt(fmt)) return TRI_EINVAL;
+    if (N < 1 || K < 1 || N >= kMaxDim || K >= kMaxDim) return TRI_EINVAL;
+    if (quant_workspace_bytes(N * K) > quant_scratch_bytes()) return TRI_EINVAL;
+    if (misaligned(W) || misaligned(Wp) || (reinterpret_cast<uintptr_t>(scale_out) & 3u)) return TRI_EALIGN;
+    void *ws = quant_scratch();
+    if (!ws) return TRI_EHIP;
+    return launch_quantize(W, N, K, fmt, Wp, scale_out, ws, stream);
+}
+
 int tri_pack2(const int8_t *W, int64_t N, int64_t K, uint8_t *Wp, hipStream_t stream)
 {
     const int rc = check_pack(W, N, K, Wp);

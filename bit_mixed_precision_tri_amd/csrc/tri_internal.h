@@ -50,6 +50,10 @@ int launch_unpack(const uint8_t *Wp, int64_t N, int64_t K, int fmt, int8_t *W, h
 int64_t quant_workspace_bytes(int64_t E);
 int launch_quantize(const float *W, int64_t N, int64_t K, int fmt, uint8_t *Wp, float *scale, void *workspace,
                     hipStream_t s);
+// The device scratch of tri_quantize_noalloc on the current device (its address from
+// hipGetSymbolAddress, taken once per device; null if the runtime reports an error), and its size.
+void *quant_scratch();
+int64_t quant_scratch_bytes();
 
 // Weight matrices that read the same activations, served by one launch (a grouped layer):
 // matrix g has N[g] rows and owns the 16-row blocks blk[g] .. blk[g+1]-1 of the grid.  A

@@ -184,6 +184,30 @@ __global__ __launch_bounds__(kThreads) void k_quant_pack16_v(const float *__rest
     }
 }
 
+// The partial sums of tri_quantize_noalloc: a file-scope device array (each device holds its own
+// copy at its own address until the process ends).  In host code `scratch` names a host-side
+// stand-in, never the device memory: kernels receive the address hipGetSymbolAddress returns.
+static __device__ __align__(256) double scratch[kMaxParts];
+
+static_assert(sizeof(scratch) == TRI_QUANTIZE_SCRATCH_BYTES, "the scratch size the header states");
+
+int64_t quant_scratch_bytes() { return (int64_t)sizeof(scratch); }
+
+void *quant_scratch()
+{
+    static std::atomic<void *> addr[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+    if (dev >= 0 && dev < kMaxDevices) {
+        void *p = addr[dev].load(std::memory_order_acquire);
+        if (p) return p;
+    }
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    if (dev >= 0 && dev < kMaxDevices) addr[dev].store(p, std::memory_order_release);
+    return p;
+}
+
 int launch_quantize(const float *W, int64_t N, int64_t K, int fmt, uint8_t *Wp, float *scale, void *workspace,
                     hipStream_t s)
 {

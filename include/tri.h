@@ -117,6 +117,21 @@ int64_t tri_quantize_workspace_bytes(int64_t N, int64_t K);
 int tri_quantize(const float *W, int64_t N, int64_t K, int fmt, uint8_t *Wp, float *scale_out,
                  void *workspace, int64_t workspace_bytes, hipStream_t stream);
 
+/* tri_quantize for callers that cannot allocate device memory or pass a workspace
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same launches and results, with the partial sums kept in a
+ * static device array of the library (16 KB per device, TRI_QUANTIZE_SCRATCH_BYTES,
+ * held until the process ends), so the call allocates nothing.  The array is
+ * enough for every N x K (at most 2048 partial sums); a matrix needing more is
+ * rejected with TRI_EINVAL.  Every call on one device shares that device's array
+ * and overwrites it (nothing in it needs to start at zero): calls that may overlap
+ * on one device (several streams, several threads) race and must be ordered by the
+ * caller.  Arguments and errors as tri_quantize without the workspace; TRI_EHIP also
+ * if the array's device address cannot be obtained. */
+enum { TRI_QUANTIZE_SCRATCH_BYTES = 16384 };
+int tri_quantize_noalloc(const float *W, int64_t N, int64_t K, int fmt, uint8_t *Wp, float *scale_out,
+                         hipStream_t stream);
+
 /* The ternary linear layer (Pith review, "What carries the argument"):
  *   Y[m][n] = fp16_rne(scale * sum_k t[n][k] * X[m][k]), fp32 accumulation.
  * X: M*K fp16 row-major (row stride K); Wp: packed weights as above; Y: M*N fp16

@@ -161,6 +161,17 @@ def test_quantize_workspace_and_argument_errors_launch_nothing():
     assert raw("tri_quantize", A, 4, 64, F2, ODD, C, A, need, s) == tri.TRI_EALIGN
     assert raw("tri_quantize", A, 4, 64, F2, B, C + 2, A, need, s) == tri.TRI_EALIGN
     assert raw("tri_quantize", A, 4, 64, F2, B, C, ODD, need, s) == tri.TRI_EALIGN
+    # the allocation-free variant: the same checks without the workspace, before any device call
+    assert tri.tri_quantize_workspace_bytes(28672, 8192) <= tri.TRI_QUANTIZE_SCRATCH_BYTES
+    assert raw("tri_quantize_noalloc", None, 4, 64, F2, B, C, s) == tri.TRI_EINVAL
+    assert raw("tri_quantize_noalloc", A, 4, 64, F2, None, C, s) == tri.TRI_EINVAL
+    assert raw("tri_quantize_noalloc", A, 4, 64, F2, B, None, s) == tri.TRI_EINVAL
+    assert raw("tri_quantize_noalloc", A, 4, 64, 2, B, C, s) == tri.TRI_EINVAL
+    for (N, K) in [(0, 64), (4, 0), (1 << 31, 64), (4, 1 << 31)]:
+        assert raw("tri_quantize_noalloc", A, N, K, F2, B, C, s) == tri.TRI_EINVAL
+    assert raw("tri_quantize_noalloc", ODD, 4, 64, F2, B, C, s) == tri.TRI_EALIGN
+    assert raw("tri_quantize_noalloc", A, 4, 64, F2, ODD, C, s) == tri.TRI_EALIGN
+    assert raw("tri_quantize_noalloc", A, 4, 64, F2, B, C + 2, s) == tri.TRI_EALIGN
 
 
 def test_fused_argument_errors_launch_nothing():
