@@ -104,16 +104,34 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
     // activations of step s: piece P = 64i + lane is piece P % RP of row P / RP, i.e. values
     // 16*(4*(s*NW + w)*XH/16 + P % RP) ... of that row: whole 128-byte lines per instruction
     const __amdgpu_buffer_rsrc_t xr = rsrc(X, __builtin_amdgcn_readfirstlane((uint32_t)((int64_t)M * K * 2)));
+    // The lane's part of each load offset does not change from step to step (a step adds the
+    // wave-uniform k of its first value); rows past M get an offset past the buffer, which
+    // reads zeros.  Values past K occur only in a wave's last live step, the one step that
+    // tests them per lane.  (The out-of-range offset is held in a register: as a literal it
+    // would be rebuilt before every select.)
+    uint32_t oob;
+    asm volatile("v_mov_b32 %0, 0x80000000" : "=v"(oob));
+    uint32_t xoff[NLD];
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+        const int P = 64 * i + lane;
+        const int row = P / RP, q = P % RP;
+        xoff[i] = row < M ? (uint32_t)(row * K + 8 * q) * 2u : oob;
+    }
     // (norm: and piece `lane` of the step's gain)
     auto load_x = [&](int s, u32x4 (&xv)[NLD], u32x4 &nv) {
+        const int kb = 4 * (s * NW + wv) * XH;   // wave-uniform
+        if (kb + 4 * XH <= K) {
 #pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-            const int P = 64 * i + lane;
-            const int row = P / RP;
-            const int k = 4 * (s * NW + wv) * XH + 8 * (P % RP);
-            const bool live = row < M && k < K;
-            const int off = live ? (int)((uint32_t)(row * K + k) * 2u) : (int)0x80000000u;
-            xv[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
+            for (int i = 0; i < NLD; ++i)
+                xv[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)(xoff[i] + 2u * (uint32_t)kb), 0, 0);
+        } else {
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) {
+                const int q = (64 * i + lane) % RP;
+                const uint32_t off = kb + 8 * q < K ? xoff[i] + 2u * (uint32_t)kb : oob;
+                xv[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)off, 0, 0);
+            }
         }
         if constexpr (NORM) {
             if (fu.gain) {
@@ -206,10 +224,12 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
             if (64 * i + lane < MT * RP) xraw[wv][64 * i + lane + (64 * i + lane) / RP] = xv[s % PD][i];
         wave_sync();
         if (s + PD < CST) load_x(s + PD, xv[s % PD], nv[s % PD]);   // refill the set just emptied
-        uint32_t x32[XH / 2];                    // row j, chunk g of the step (zero past the tile's rows)
+        // row j, chunk g of the step (tiles of fewer than 16 rows: A rows past the tile repeat its
+        // rows, and the D rows they give are never read)
+        uint32_t x32[XH / 2];
 #pragma unroll
         for (int q = 0; q < XH / 8; ++q) {
-            const u32x4 v = j < MT ? xraw[wv][j * RPP + (XH / 8) * g + q] : u32x4{0u, 0u, 0u, 0u};
+            const u32x4 v = xraw[wv][(j % MT) * RPP + (XH / 8) * g + q];
             x32[4 * q] = v[0]; x32[4 * q + 1] = v[1]; x32[4 * q + 2] = v[2]; x32[4 * q + 3] = v[3];
         }
         if constexpr (NORM) {
