@@ -255,7 +255,7 @@ def main():
     ap.add_argument("--skip-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--floor", action="store_true",
                     help="only the decode floor: empty and loads-only probes on the decode grid, streaming reads")
-    ap.add_argument("--profile", choices=["decode", "copy", "prefill", "batched", "floor"],
+    ap.add_argument("--profile", choices=["decode", "copy", "prefill", "batched", "floor", "block"],
                     help="only launch one workload a few times (for rocprofv3 --pmc runs)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -730,11 +730,17 @@ def profile_mode(which):
     from bit_mixed_precision_tri_amd import configs
     if which == "decode":
         cfg = configs.DECODE
-        layers = [Layer(cfg["workload_id"], li, 1, N, K, tri.TRI_FMT_2BIT)
-                  for li, (name, K, N) in enumerate(cfg["shapes"])]
-        for _ in range(20):
-            for L in layers:
-                L.launch()
+        for fmt in (tri.TRI_FMT_2BIT, tri.TRI_FMT_1P6BIT):
+            layers = [Layer(cfg["workload_id"], li + (0 if fmt == tri.TRI_FMT_2BIT else 20), 1, N, K, fmt)
+                      for li, (name, K, N) in enumerate(cfg["shapes"])]
+            for _ in range(20):
+                for L in layers:
+                    L.launch()
+            torch.cuda.synchronize()
+            del layers
+            torch.cuda.empty_cache()
+    elif which == "block":
+        bench_block(Clock())
     elif which == "prefill":
         cfg = configs.PREFILL
         name, K, N = cfg["shapes"][0]

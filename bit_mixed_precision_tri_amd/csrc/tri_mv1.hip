@@ -66,6 +66,13 @@ __device__ __forceinline__ float4_t mfma(const u32x4 a, const u32x4 b, float4_t 
 
 }  // namespace
 
+// LDS of the staged A operands of a workgroup (the layouts of k_mv1's xa and xb).
+template <int FMT, int NW, int CST, int MR>
+constexpr int xa_bytes()
+{
+    return FMT == TRI_FMT_2BIT ? NW * 4 * CST * MR * (8 + (MR == 4 ? 1 : 0)) * 16 : NW * MR * (4 * CST * 10 + 1) * 16;
+}
+
 // Block loop: outputs held in LDS before they are written (an even count), and the blocks per
 // resident workgroup slot from which the loop pays.
 constexpr int kPsOut = 16;
@@ -93,11 +100,15 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
     constexpr int PIECES = XH / 8;               // 16-byte activation pieces per chunk
     constexpr int NLD = (NCH * PIECES + 63) / 64;   // whole-line activation loads per lane
     static_assert(NCH <= 64, "chunks per wave");
-    // per wave: A operands of its chunks, per activation row (four rows: one 16-byte pad per row,
-    // so the rows one read instruction touches fall in distinct banks)
+    // per wave: A operands of its chunks, per activation row.  2-bit: chunk-major (four rows: one
+    // 16-byte pad per row, so the rows one read instruction touches fall in distinct banks).
+    // 1.6-bit: row-major, chunk after chunk, each row padded by 16 bytes for the same reason; a
+    // row is staged in place (the ten raw pieces of chunk l occupy the 160 bytes its ten A
+    // operands will), so no separate bounce buffer is needed.
     constexpr int NOPP = MR == 4 ? NOP + 1 : NOP;
-    __shared__ u32x4 xa[NW][NCH][MR][NOPP];
-    __shared__ u32x4 xraw[TWO ? 1 : NW][TWO ? 1 : NCH * PIECES];   // 1.6-bit: raw pieces
+    constexpr int XBR = NCH * NOP + 1;           // 1.6-bit: 16-byte slots per row (+ pad)
+    __shared__ u32x4 xa[TWO ? NW : 1][TWO ? NCH : 1][TWO ? MR : 1][TWO ? NOPP : 1];
+    __shared__ u32x4 xb[TWO ? 1 : NW][TWO ? 1 : MR][TWO ? 1 : XBR];
     // per wave and activation row: the 16 outputs of each block, sum x (, sum x^2)
     __shared__ float red[PS ? 2 : 1][NW][MR][16 * RB + (NORM ? 2 : 1)];   // (block loop: two, alternating)
     __shared__ float yst[PS ? kPsOut : 1][MR][16];   // block loop: outputs not yet written
@@ -208,26 +219,25 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
                 }
             }
     } else {
-        // the pairing of a 40-value half spans ten pieces: bounce the raw pieces through LDS,
-        // one activation row at a time
+        // the pairing of a 40-value half spans ten pieces: bounce the raw pieces through the
+        // row's own slots (piece P of the wave's pieces to slot P), then lane l reads the ten
+        // pieces of chunk l and overwrites the same ten slots with its A operands (no other lane
+        // reads them after the barrier)
 #pragma unroll
-        for (int r = 0; r < MR; ++r) {
-            if (r > 0) {                         // the previous row's pieces have been read
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            }
+        for (int r = 0; r < MR; ++r)
 #pragma unroll
             for (int i = 0; i < NLD; ++i)
-                if (64 * i + lane < NCH * PIECES) xraw[wv][64 * i + lane] = xv[r][i];
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                if (64 * i + lane < NCH * PIECES) xb[wv][r][64 * i + lane] = xv[r][i];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int r = 0; r < MR; ++r) {
             if (lane < NCH) {
                 uint32_t x32[40];
 #pragma unroll
                 for (int q = 0; q < 10; ++q) {
-                    const u32x4 v = xraw[wv][10 * lane + q];
+                    const u32x4 v = xb[wv][r][10 * lane + q];
                     x32[4 * q] = v[0]; x32[4 * q + 1] = v[1]; x32[4 * q + 2] = v[2]; x32[4 * q + 3] = v[3];
                 }
 #pragma unroll
@@ -241,7 +251,7 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
                             av[qq] = (e & 1) ? pair_halves<1>(x32[(e >> 1) + 20], x32[e >> 1])
                                              : pair_halves<0>(x32[(e >> 1) + 20], x32[e >> 1]);
                         }
-                        xa[wv][lane][r][2 * p + hh] = av;
+                        xb[wv][r][10 * lane + 2 * p + hh] = av;
                     }
             }
         }
@@ -308,7 +318,9 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
             // wave-uniform: no chunk of this step is live (the block loop contracts such steps,
             // whose activations are zero: a skipped step would leave its loads pending)
             if (!PS && 4 * (s * NW + wv) >= C) break;
-            const u32x4 *asrc = &xa[wv][4 * s + g][j % MR][0];   // A row j: activation row j % MR
+            const u32x4 *asrc;                   // A row j: activation row j % MR
+            if constexpr (TWO) asrc = &xa[wv][4 * s + g][j % MR][0];
+            else asrc = &xb[wv][j % MR][(4 * s + g) * NOP];
             u32x4 a[NOP];
 #pragma unroll
             for (int p = 0; p < NOP; ++p) a[p] = asrc[p];
@@ -416,7 +428,7 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
 template <int FMT, int NW, int CST, int MR>
 static bool launch_loop(const uint16_t *X, const Groups &gr, int M, int K, int C, hipStream_t s, const Fusion &f)
 {
-    constexpr int kXaBytes = NW * 4 * CST * MR * ((FMT == TRI_FMT_2BIT ? 8 : 10) + (MR == 4 ? 1 : 0)) * 16;
+    constexpr int kXaBytes = xa_bytes<FMT, NW, CST, MR>();
     if constexpr (NW > 8 || (MR > 1 && kXaBytes > (MR == 4 ? 120 : 100) * 1024)) {   // (the staged operands' LDS, as below)
         return false;
     } else {
@@ -435,7 +447,7 @@ static bool launch_gl(const uint16_t *X, const Groups &gr, int M, int K, int C, 
     // several activation rows: only while the staged A operands of the workgroup stay below
     // 100 KB of LDS (120 KB at four rows, 136 KB at sixteen waves, whose registers hold one
     // workgroup per CU anyway)
-    constexpr int kXaBytes = NW * 4 * CST * MR * ((FMT == TRI_FMT_2BIT ? 8 : 10) + (MR == 4 ? 1 : 0)) * 16;
+    constexpr int kXaBytes = xa_bytes<FMT, NW, CST, MR>();
     if constexpr (MR > 1 && kXaBytes > (NW == 16 ? 136 : MR == 4 ? 120 : 100) * 1024) {
         return false;
     } else {
@@ -534,10 +546,10 @@ static bool launch_fmt(const uint16_t *X, const Groups &gr, int M, int K, int C,
     case 8: return launch_cfg<FMT, 8, 8, MR>(X, gr, M, K, C, s, fu);
     default: break;
     }
-    // sixteen waves (one activation row; two for 2-bit, whose activations need no bounce buffer);
-    // the staged activations of a workgroup must fit in LDS.  (The pair variant would exceed the
-    // registers a wave has at sixteen waves: longer rows are not paired.)
-    if constexpr (MR == 1 || (MR == 2 && FMT == TRI_FMT_2BIT)) {
+    // sixteen waves (one or two activation rows); the staged activations of a workgroup must fit
+    // in LDS.  (The pair variant would exceed the registers a wave has at sixteen waves: longer
+    // rows are not paired.)
+    if constexpr (MR <= 2) {
         if (fu && fu->pair) return false;
         const int cst16 = (C + 63) / 64;
         if (cst16 <= 6) return launch_cfg<FMT, 16, 6, MR>(X, gr, M, K, C, s, fu);
