@@ -77,6 +77,9 @@ constexpr int xa_bytes()
 // resident workgroup slot from which the loop pays.
 constexpr int kPsOut = 16;
 constexpr int kLoopBlocksPerSlot = 2;
+// (a sixteen-wave loop for one-row 2-bit decode from three blocks per resident workgroup: at two
+// it lost to the eight-wave one-shot grid, 11008 -> 8192: 7.19 -> 7.86 us)
+constexpr int kTallBlocksPerSlot = 3;
 
 template <int FMT, int NW, int CST, int GL, bool ONE, int MR, int RB, bool PS>
 __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X, const Groups gr, int M, int K, int C,
@@ -429,7 +432,10 @@ template <int FMT, int NW, int CST, int MR>
 static bool launch_loop(const uint16_t *X, const Groups &gr, int M, int K, int C, hipStream_t s, const Fusion &f)
 {
     constexpr int kXaBytes = xa_bytes<FMT, NW, CST, MR>();
-    if constexpr (NW > 8 || (MR > 1 && kXaBytes > (MR == 4 ? 120 : 100) * 1024)) {   // (the staged operands' LDS, as below)
+    // (eight waves, or sixteen of up to four steps at one 2-bit row: more would spill the second
+    // register set; the staged operands' LDS as below)
+    if constexpr ((NW > 8 && !(NW == 16 && CST <= 4 && MR == 1 && FMT == TRI_FMT_2BIT)) ||
+                  (MR > 1 && kXaBytes > (MR == 4 ? 120 : 100) * 1024)) {
         return false;
     } else {
         if (gr.G != 1 || (int64_t)gr.N[0] * C * 16 >= ((int64_t)1 << 31)) return false;
@@ -439,6 +445,17 @@ static bool launch_loop(const uint16_t *X, const Groups &gr, int M, int K, int C
                            C, f);
         return true;
     }
+}
+
+// Matrices of the group with at least kTallBlocksPerSlot 16-row blocks per workgroup of the NW-wave
+// block loop that the device holds at once.
+template <int FMT, int NW, int CST>
+static int tall_count(const Groups &gr)
+{
+    const int64_t resident = (int64_t)resident_per_cu<k_mv1<FMT, NW, CST, 0, true, 1, 1, true>>(64 * NW) * cu_count();
+    int n = 0;
+    for (int g = 0; g < gr.G; ++g) n += (int64_t)(gr.blk[g + 1] - gr.blk[g]) >= kTallBlocksPerSlot * resident;
+    return n;
 }
 
 template <int FMT, int NW, int CST, int GL, int MR, int RB>
@@ -535,6 +552,33 @@ static bool launch_fmt(const uint16_t *X, const Groups &gr, int M, int K, int C,
         }
     }
     const int cst8 = (C + 31) / 32;              // chunk-steps with 8 waves (4 chunks per step and wave)
+    // Tall 2-bit matrices with rows of five to eight steps per wave of eight (8192 < K <= 16384) at one
+    // row: sixteen waves of three or four steps, whose block loop over the matrix keeps four waves per
+    // SIMD instead of two (11008 -> 14336: 12.9 -> 11.9 us, 16384 -> 16384: 20.5 -> 17.2 us; at two blocks
+    // per resident workgroup it loses, 11008 -> 8192: 7.2 -> 7.9 us, and a one-shot grid gains nothing
+    // on sixteen waves, so shorter matrices keep eight).  A matrix is tall when it has at least
+    // kTallBlocksPerSlot blocks per resident sixteen-wave workgroup;
+    // the choice is made per matrix, so a single, a grouped and a residual launch of it take the same
+    // kernel (bitwise equal results), and a group that mixes tall and short matrices runs one launch per
+    // matrix.  The norm and pair glue keep eight waves.
+    if constexpr (FMT == TRI_FMT_2BIT && MR == 1) {
+        if (!glue_bits(fu) && cst8 >= 5 && cst8 <= 8) {
+            const int tall = cst8 <= 6 ? tall_count<FMT, 16, 3>(gr) : tall_count<FMT, 16, 4>(gr);
+            if (tall == gr.G)
+                return cst8 <= 6 ? launch_cfg<FMT, 16, 3, 1>(X, gr, M, K, C, s, fu)
+                                 : launch_cfg<FMT, 16, 4, 1>(X, gr, M, K, C, s, fu);
+            if (tall > 0) {                      // (tall and short matrices in one group: one launch each)
+                for (int g = 0; g < gr.G; ++g) {
+                    const Groups one = make_groups(1, &gr.Wp[g], &gr.scale[g], &gr.N[g], &gr.Y[g]);
+                    Fusion f1 = fu ? *fu : Fusion{};
+                    f1.res[0] = f1.res[g];
+                    for (int q = 1; q < kMaxGroups; ++q) f1.res[q] = nullptr;
+                    if (!launch_fmt<FMT, MR>(X, one, M, K, C, s, fu ? &f1 : nullptr)) return false;
+                }
+                return true;
+            }
+        }
+    }
     switch (cst8) {
     case 1: return launch_cfg<FMT, 8, 1, MR>(X, gr, M, K, C, s, fu);
     case 2: return launch_cfg<FMT, 8, 2, MR>(X, gr, M, K, C, s, fu);

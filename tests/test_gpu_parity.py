@@ -428,7 +428,9 @@ TALL = [(tri.TRI_FMT_2BIT, 1, 40007, 4096), (tri.TRI_FMT_2BIT, 2, 40007, 4096),
         (tri.TRI_FMT_1P6BIT, 3, 30011, 8192), (tri.TRI_FMT_1P6BIT, 4, 40003, 4096),
         # the largest staged-operand instances of the loop: four rows over six (2-bit) and five
         # (1.6-bit) steps per wave, 563 blocks against 512 resident workgroups
-        (tri.TRI_FMT_2BIT, 4, 9000, 11008), (tri.TRI_FMT_1P6BIT, 4, 9000, 12000)]
+        (tri.TRI_FMT_2BIT, 4, 9000, 11008), (tri.TRI_FMT_1P6BIT, 4, 9000, 12000),
+        # one 2-bit row of 8192 < K <= 16384: the loop on sixteen waves of three and four steps
+        (tri.TRI_FMT_2BIT, 1, 40007, 11008), (tri.TRI_FMT_2BIT, 1, 20011, 16384)]
 
 
 @pytest.mark.parametrize("fmt,M,N,K", TALL)
@@ -450,3 +452,24 @@ def test_block_loop_tall_matrices(fmt, M, N, K):
               torch.empty((M, 64), dtype=torch.float16, device="cuda")]
         tri.tri_linear_grouped(Xd, [Wp, Wp2], [s, 0.03], M, [N, 64], K, fmt, Ys)
         np.testing.assert_array_equal(Y, host(Ys[0]))
+
+
+def test_grouped_tall_matrices_same_as_single():
+    """Two tall 2-bit matrices (at least three 16-row blocks per resident sixteen-wave workgroup) of
+    rows between 8192 and 16384 trits at one activation row: alone each runs the sixteen-wave block
+    loop, together the sixteen-wave one-shot grid; the outputs are the oracle's within the bound and
+    bitwise the same either way."""
+    import torch
+    M, K, Ns = 1, 11008, [12300, 12400]
+    X = synth.activations(synth.rng_for(530, 1, synth.STREAM_X), M, K)
+    Ws = [synth.trits(synth.rng_for(530, 10 + g, synth.STREAM_W), n, K) for g, n in enumerate(Ns)]
+    scales = [0.02, -0.035]
+    Xd = cuda(X)
+    Wps = [tri.pack(cuda(W), F2) for W in Ws]
+    Ys = [torch.empty((M, n), dtype=torch.float16, device="cuda") for n in Ns]
+    say("grouped tall 2 x ~12300 rows K=%d" % K)
+    tri.tri_linear_grouped(Xd, Wps, scales, M, Ns, K, F2, Ys)
+    for g, (W, s, Y) in enumerate(zip(Ws, scales, Ys)):
+        Yh = host(Y)
+        check_layer(Yh, X, W, s, "grouped tall g=%d" % g)
+        np.testing.assert_array_equal(Yh, host(tri.linear(Xd, Wps[g], s, K, F2)))
