@@ -16,15 +16,16 @@
 // s, where lane (g = lane/16, j = lane%16) reads 16-byte chunk c = 4*(s*NW + w) + g of row j of
 // every block and supplies the activations of row j of X (as A operand) for the same chunk.  All weight chunks
 // of the wave are requested at the start.  The activations of a step -- four consecutive
-// chunks of every activation row -- are read with whole-line loads one step ahead, bounced
-// through the wave's LDS slot to the lanes that use them, and permuted there into the
-// pairing of the decoded weights (2-bit: trits (16v+p, 16v+8+p); 1.6-bit: (5q+p, 5q+40+p)).
-// The waves' partial tiles are added in LDS in a fixed order (no atomics).
+// chunks of every activation row -- are read with whole-line buffer loads that write straight
+// into one of the wave's LDS slots (gfx950 loads to LDS: no registers, no LDS write
+// instructions), up to two steps ahead; each lane then reads its row's pieces and permutes them
+// into the pairing of the decoded weights (2-bit: trits (16v+p, 16v+8+p); 1.6-bit:
+// (5q+p, 5q+40+p)).  The waves' partial tiles are added in LDS in a fixed order (no atomics).
 //
 // Block glue.  Every variant adds an optional residual to the fp32 results before rounding.
-// Norm variant (GL & kGlueNorm): after the bounce each lane adds the squares of its row's
-// values and multiplies them by the norm gain (rounded to fp16), which travels as one more
-// row of the wave's LDS slot; the 1/rms factor of each row scales its results.  Pair variant
+// Norm variant (GL & kGlueNorm): each lane adds the squares of its row's values and multiplies
+// them by the norm gain (rounded to fp16), which is loaded into the same slot behind the
+// activations; the 1/rms factor of each row scales its results.  Pair variant
 // (GL & kGluePair): the workgroup also reads the same 16 rows of a second matrix, contracts
 // them with the same A operands, and writes fp16(silu(y0) * y1) as its only output.
 #include "tri_device.h"
@@ -47,11 +48,35 @@ __device__ __forceinline__ float4_t mfma(const u32x4 a, const u32x4 b, float4_t 
                                                   0, 0);
 }
 
-__device__ __forceinline__ void wave_sync()
+typedef __attribute__((address_space(3))) char *lds_ptr_t;
+
+// Position of piece q of activation row r within its row of an LDS slot.  Rows of 32 pieces
+// XOR the position with r, so the sixteen rows that one read instruction touches (one piece
+// each) fall in sixteen distinct 16-byte bank groups; rows of 40 pieces do the same within
+// their first 32 and last 8 pieces.  (The map is its own inverse.)
+template <int RP>
+__device__ __forceinline__ int swz(int r, int q)
 {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if constexpr (RP == 32) return q ^ (r & 15);
+    else return q < 32 ? q ^ (r & 15) : 32 + ((q - 32) ^ (r & 7));
+}
+
+// s_waitcnt vmcnt(n): wait until at most n vector-memory loads of the wave are outstanding
+// (the counter retires in issue order); n must fold to a constant.
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | (((N >> 4) & 3) << 14));   // (expcnt, lgkmcnt: no wait)
+}
+template <int N = 0>
+__device__ __forceinline__ void wait_vm_upto(int n)
+{
+    if constexpr (N < 63) {
+        if (n <= N) wait_vm<N>();
+        else wait_vm_upto<N + 1>(n);
+    } else {
+        wait_vm<63>();
+    }
 }
 
 }  // namespace
@@ -83,14 +108,18 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
     constexpr int NCLS = TWO ? 6 : (QT ? 4 : 2);   // accumulators: position classes (2-bit), sums (1.6-bit)
     constexpr int RP = 4 * XH / 8;               // 16-byte pieces of one row per step (32 or 40)
     constexpr int NLD = (MT * RP + 63) / 64;     // whole-line activation loads per lane and step
-    constexpr int RPP = RP + 1;                  // padded row stride: the 16 rows a read touches fall in distinct banks
-    constexpr int XROWS = MT + (NORM ? 1 : 0);   // (+ the norm gain of the step's chunks)
-    // per wave: one step's activations, row-major; after the last step the same LDS holds the
-    // per-wave partial tiles [row m][column (block r, row j)], + sum x (+ sum x^2)
+    // per wave: PD slots of one step's activations each (piece q of row r at r * RP + swz(r, q);
+    // every load instruction fills 64 pieces, so a slot holds NLD * 64, + 64 for the norm gain).
+    // Two slots where eight waves' take at most 128 KB (at most 64 KB for four waves, which
+    // share a CU two at a time), else one; one for the glue variants, whose fused launches
+    // have grids of several workgroups per CU.  After the last step the same LDS holds the
+    // per-wave partial tiles [row m][column (block r, row j)], + sum x (+ sum x^2).
+    constexpr int SLOT = (NLD + (NORM ? 1 : 0)) * 64;
+    constexpr int PD = GL == 0 && NW * 2 * SLOT * 16 <= (NW <= 4 ? 64 : 128) * 1024 ? 2 : 1;
     constexpr int RCOL = 16 * RB + (NORM ? 2 : 1);
-    constexpr int XRAW_B = NW * XROWS * RPP * 16, RED_B = NW * 16 * RCOL * 4;
-    __shared__ u32x4 smem[(XRAW_B > RED_B ? XRAW_B : RED_B) / 16];
-    u32x4 (*xraw)[XROWS * RPP] = reinterpret_cast<u32x4 (*)[XROWS * RPP]>(smem);
+    constexpr int XS_B = NW * PD * SLOT * 16, RED_B = NW * 16 * RCOL * 4;
+    __shared__ u32x4 smem[(XS_B > RED_B ? XS_B : RED_B) / 16];
+    u32x4 (*xs)[PD][SLOT] = reinterpret_cast<u32x4 (*)[PD][SLOT]>(smem);
     float (*red)[16][RCOL] = reinterpret_cast<float (*)[16][RCOL]>(smem);
     __shared__ float red1[PAIR ? NW : 1][16][17];    // pair: the second matrix's partial tile
 
@@ -101,8 +130,9 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
     const int n0 = ((int)blockIdx.x - grp.first) * 16 * RB;
     const int64_t S = (int64_t)C * 16;
 
-    // activations of step s: piece P = 64i + lane is piece P % RP of row P / RP, i.e. values
-    // 16*(4*(s*NW + w)*XH/16 + P % RP) ... of that row: whole 128-byte lines per instruction
+    // activations of step s: load instruction i, lane l fills slot position P = 64i + l, that is
+    // row P / RP at position P % RP, with piece swz(row, P % RP) of the row's step (values
+    // 8 q ... of the step's 4 XH): whole 128-byte lines per instruction
     const __amdgpu_buffer_rsrc_t xr = rsrc(X, __builtin_amdgcn_readfirstlane((uint32_t)((int64_t)M * K * 2)));
     // The lane's part of each load offset does not change from step to step (a step adds the
     // wave-uniform k of its first value); rows past M get an offset past the buffer, which
@@ -115,31 +145,29 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
         const int P = 64 * i + lane;
-        const int row = P / RP, q = P % RP;
+        const int row = P / RP, q = swz<RP>(row, P % RP);
         xoff[i] = row < M ? (uint32_t)(row * K + 8 * q) * 2u : oob;
     }
-    // (norm: and piece `lane` of the step's gain)
-    auto load_x = [&](int s, u32x4 (&xv)[NLD], u32x4 &nv) {
+    // step s into slot s % PD (norm: and piece `lane` of the step's gain behind it; without a
+    // gain the resource is empty and the pieces read as zero, so every step issues the same
+    // number of loads)
+    const __amdgpu_buffer_rsrc_t gn = rsrc(fu.gain, NORM && fu.gain ? (uint32_t)K * 2u : 0u);
+    auto load_x = [&](int s) {
         const int kb = 4 * (s * NW + wv) * XH;   // wave-uniform
-        if (kb + 4 * XH <= K) {
+        const lds_ptr_t dst = (lds_ptr_t)&xs[wv][s % PD][0];
+        const bool whole = kb + 4 * XH <= K;
 #pragma unroll
-            for (int i = 0; i < NLD; ++i)
-                xv[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)(xoff[i] + 2u * (uint32_t)kb), 0, 0);
-        } else {
-#pragma unroll
-            for (int i = 0; i < NLD; ++i) {
-                const int q = (64 * i + lane) % RP;
-                const uint32_t off = kb + 8 * q < K ? xoff[i] + 2u * (uint32_t)kb : oob;
-                xv[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)off, 0, 0);
-            }
+        for (int i = 0; i < NLD; ++i) {
+            const int P = 64 * i + lane;
+            const int q = swz<RP>(P / RP, P % RP);
+            const uint32_t off = (whole || kb + 8 * q < K) ? xoff[i] + 2u * (uint32_t)kb : oob;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, dst + 1024 * i, 16, (int)off, 0, 0, 0);
         }
         if constexpr (NORM) {
-            if (fu.gain) {
-                const int k = 4 * (s * NW + wv) * XH + 8 * lane;
-                nv = __builtin_amdgcn_raw_buffer_load_b128(
-                    rsrc(fu.gain, (uint32_t)K * 2u), (lane < RP && k < K) ? (int)((uint32_t)k * 2u) : (int)0x80000000u,
-                    0, 0);
-            }
+            const int k = kb + 8 * lane;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(gn, dst + 1024 * NLD, 16,
+                                                    (lane < RP && k < K) ? (int)((uint32_t)k * 2u) : (int)0x80000000u,
+                                                    0, 0, 0);
         }
     };
 
@@ -183,14 +211,11 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
     };
     float4_t accx = zero4;                       // sum_k X[m][k] in every column of the tile
     float xsq = 0.f;                             // norm: sum of x^2 over this lane's values of row j
-    // the activations of PD steps are in flight at once (a ring of register sets).  The first
-    // PD steps' activations are requested before the weights: the load counter is in order,
-    // so the first steps' bounce and permutation overlap the weight stream instead of waiting
-    // behind it (two steps measured best; deeper rings gained about 1%)
-    constexpr int PD = 2;
-    u32x4 xv[PD][NLD], nv[PD];
+    // the activations of PD steps are in flight at once.  The first PD steps' activations are
+    // requested before the weights: the load counter is in order, so the first steps'
+    // permutation overlaps the weight stream instead of waiting behind it
 #pragma unroll
-    for (int t = 0; t < PD; ++t) load_x(t, xv[t], nv[t]);
+    for (int t = 0; t < PD; ++t) load_x(t);
     // every weight chunk of the wave, all in flight at once
     const int rows_here = min(16 * RB, N - n0);
     const __amdgpu_buffer_rsrc_t wr =
@@ -215,21 +240,24 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
 #pragma unroll
     for (int s = 0; s < CST; ++s) {
         if (4 * (s * NW + wv) >= C) break;       // wave-uniform: no chunk of this step is live
-        // bounce the step's raw activations to the lanes that use them, then permute there
-        if constexpr (NORM) {
-            if (fu.gain && lane < RP) xraw[wv][MT * RPP + lane] = nv[s % PD];
+        // wait for this step's pieces: loads issued after them are the later prefetched steps,
+        // the weights (while s < PD) and the refills of the steps after s
+        {
+            constexpr int NWL = CST * RB + (PAIR ? CST : 0), NX = NLD + (NORM ? 1 : 0);
+            int after = 0;
+            for (int u = s + 1; u < PD; ++u) after += NX;
+            if (s < PD) after += NWL;
+            for (int t = s - PD + 1 > 0 ? s - PD + 1 : 0; t < s; ++t) after += t + PD < CST ? NX : 0;
+            wait_vm_upto(after);
         }
-#pragma unroll
-        for (int i = 0; i < NLD; ++i)
-            if (64 * i + lane < MT * RP) xraw[wv][64 * i + lane + (64 * i + lane) / RP] = xv[s % PD][i];
-        wave_sync();
-        if (s + PD < CST) load_x(s + PD, xv[s % PD], nv[s % PD]);   // refill the set just emptied
         // row j, chunk g of the step (tiles of fewer than 16 rows: A rows past the tile repeat its
         // rows, and the D rows they give are never read)
+        const u32x4 *slot = &xs[wv][s % PD][0];
+        const int row = j % MT;
         uint32_t x32[XH / 2];
 #pragma unroll
         for (int q = 0; q < XH / 8; ++q) {
-            const u32x4 v = xraw[wv][(j % MT) * RPP + (XH / 8) * g + q];
+            const u32x4 v = slot[row * RP + swz<RP>(row, (XH / 8) * g + q)];
             x32[4 * q] = v[0]; x32[4 * q + 1] = v[1]; x32[4 * q + 2] = v[2]; x32[4 * q + 3] = v[3];
         }
         if constexpr (NORM) {
@@ -238,13 +266,14 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
             if (fu.gain) {
 #pragma unroll
                 for (int q = 0; q < XH / 8; ++q) {
-                    const u32x4 gq = xraw[wv][MT * RPP + (XH / 8) * g + q];   // the same for every row
+                    const u32x4 gq = slot[NLD * 64 + (XH / 8) * g + q];   // the same for every row
 #pragma unroll
                     for (int e = 0; e < 4; ++e) x32[4 * q + e] = mul2(x32[4 * q + e], gq[e]);
                 }
             }
         }
-        wave_sync();                             // the slot may be refilled at the next step
+        __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): the slot's reads are done before it is refilled
+        if (s + PD < CST) load_x(s + PD);
         u32x4 a[NOP];
         if constexpr (TWO) {
 #pragma unroll
