@@ -155,13 +155,19 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
     auto load_x = [&](int s) {
         const int kb = 4 * (s * NW + wv) * XH;   // wave-uniform
         const lds_ptr_t dst = (lds_ptr_t)&xs[wv][s % PD][0];
-        const bool whole = kb + 4 * XH <= K;
+        if (kb + 4 * XH <= K) {                  // (wave-uniform: only a wave's last live step tests K per lane)
 #pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-            const int P = 64 * i + lane;
-            const int q = swz<RP>(P / RP, P % RP);
-            const uint32_t off = (whole || kb + 8 * q < K) ? xoff[i] + 2u * (uint32_t)kb : oob;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, dst + 1024 * i, 16, (int)off, 0, 0, 0);
+            for (int i = 0; i < NLD; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, dst + 1024 * i, 16, (int)(xoff[i] + 2u * (uint32_t)kb), 0,
+                                                        0, 0);
+        } else {
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) {
+                const int P = 64 * i + lane;
+                const int q = swz<RP>(P / RP, P % RP);
+                const uint32_t off = kb + 8 * q < K ? xoff[i] + 2u * (uint32_t)kb : oob;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, dst + 1024 * i, 16, (int)off, 0, 0, 0);
+            }
         }
         if constexpr (NORM) {
             const int k = kb + 8 * lane;
@@ -241,7 +247,8 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
     for (int s = 0; s < CST; ++s) {
         if (4 * (s * NW + wv) >= C) break;       // wave-uniform: no chunk of this step is live
         // wait for this step's pieces: loads issued after them are the later prefetched steps,
-        // the weights (while s < PD) and the refills of the steps after s
+        // the weights (while s < PD) and the refills (issued at the ends of the earlier steps) of
+        // the steps after s
         {
             constexpr int NWL = CST * RB + (PAIR ? CST : 0), NX = NLD + (NORM ? 1 : 0);
             int after = 0;
@@ -272,8 +279,6 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
                 }
             }
         }
-        __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): the slot's reads are done before it is refilled
-        if (s + PD < CST) load_x(s + PD);
         u32x4 a[NOP];
         if constexpr (TWO) {
 #pragma unroll
@@ -302,6 +307,12 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
 #pragma unroll
         for (int r = 0; r < RB; ++r) contract(a, wq[r][s], acc[r]);
         if constexpr (PAIR) contract(a, wq1[s], acc1);
+        // refill the slot with step s + PD once its reads are done.  (Issued after the contraction:
+        // the compiler's own waits for the weight registers do not count the loads to LDS, so a
+        // refill issued earlier would be waited for with them -- measured 4% slower at 11008 -> 4096,
+        // M = 16.)
+        __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0)
+        if (s + PD < CST) load_x(s + PD);
     }
 
     // merge classes: lane (g, j) holds rows 4g + e of column j (of D and of the sums of X)
