@@ -362,7 +362,7 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
                 float sq = 0.f;
 #pragma unroll
                 for (int w = 0; w < NW; ++w) sq += rd[w][0][16 * RB + 1];
-                rinv = 1.f / sqrtf(sq / (float)K + fu.eps);
+                rinv = __builtin_amdgcn_rsqf(sq * __builtin_amdgcn_rcpf((float)K) + fu.eps);   // (v_rsq, v_rcp: about 1 ulp)
             }
             float y = (sd * 16777216.0f - sx) * scale * rinv;
             if constexpr (PAIR) {

@@ -111,11 +111,11 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
     // per wave: PD slots of one step's activations each (piece q of row r at r * RP + swz(r, q);
     // every load instruction fills 64 pieces, so a slot holds NLD * 64, + 64 for the norm gain).
     // Two slots where eight waves' take at most 128 KB (at most 64 KB for four waves, which
-    // share a CU two at a time), else one; one for the glue variants, whose fused launches
-    // have grids of several workgroups per CU.  After the last step the same LDS holds the
-    // per-wave partial tiles [row m][column (block r, row j)], + sum x (+ sum x^2).
+    // share a CU two at a time), else one; one for the pair variant, whose fused launches have
+    // grids of several workgroups per CU.  After the last step the same LDS holds the per-wave
+    // partial tiles [row m][column (block r, row j)], + sum x (+ sum x^2).
     constexpr int SLOT = (NLD + (NORM ? 1 : 0)) * 64;
-    constexpr int PD = GL == 0 && NW * 2 * SLOT * 16 <= (NW <= 4 ? 64 : 128) * 1024 ? 2 : 1;
+    constexpr int PD = !PAIR && NW * 2 * SLOT * 16 <= (NW <= 4 ? 64 : 128) * 1024 ? 2 : 1;
     constexpr int RCOL = 16 * RB + (NORM ? 2 : 1);
     constexpr int XS_B = NW * PD * SLOT * 16, RED_B = NW * 16 * RCOL * 4;
     __shared__ u32x4 smem[(XS_B > RED_B ? XS_B : RED_B) / 16];
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
                 float sq = 0.f;
 #pragma unroll
                 for (int w = 0; w < NW; ++w) sq += red[w][m][16 * RB + 1];
-                rinv = 1.f / sqrtf(sq / (float)K + fu.eps);
+                rinv = __builtin_amdgcn_rsqf(sq * __builtin_amdgcn_rcpf((float)K) + fu.eps);   // (v_rsq, v_rcp: about 1 ulp)
             }
             float y = (sd * 16777216.0f - sx) * scale * rinv;
             if constexpr (PAIR) {
