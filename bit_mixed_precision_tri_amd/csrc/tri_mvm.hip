@@ -87,7 +87,7 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
 {
     constexpr bool NORM = (GL & kGlueNorm) != 0;
     constexpr bool PAIR = (GL & kGluePair) != 0;
-    static_assert(!PAIR || RB == 1, "the pair variant owns one 16-row block of each matrix per workgroup");
+    static_assert(!PAIR || RB <= 2, "the pair variant owns one or two 16-row blocks of each matrix per workgroup");
     const GroupSel grp = select_group<ONE>(gr, fu, (int)blockIdx.x);
     const uint8_t *__restrict__ Wp = grp.Wp;
     const float scale = grp.scale;
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
     __shared__ u32x4 smem[(XS_B > RED_B ? XS_B : RED_B) / 16];
     u32x4 (*xs)[PD][SLOT] = reinterpret_cast<u32x4 (*)[PD][SLOT]>(smem);
     float (*red)[16][RCOL] = reinterpret_cast<float (*)[16][RCOL]>(smem);
-    __shared__ float red1[PAIR ? NW : 1][16][17];    // pair: the second matrix's partial tile
+    __shared__ float red1[PAIR ? NW : 1][16][PAIR ? 16 * RB + 1 : 1];   // pair: the second matrix's partial tiles
 
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar descriptors)
@@ -183,9 +183,11 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
     for (int r = 0; r < RB; ++r)
 #pragma unroll
         for (int c = 0; c < NCLS; ++c) acc[r][c] = zero4;
-    float4_t acc1[PAIR ? NCLS : 1];              // pair: the second matrix
+    float4_t acc1[PAIR ? RB : 1][PAIR ? NCLS : 1];   // pair: the second matrix
 #pragma unroll
-    for (int c = 0; c < (PAIR ? NCLS : 1); ++c) acc1[c] = zero4;
+    for (int r = 0; r < (PAIR ? RB : 1); ++r)
+#pragma unroll
+        for (int c = 0; c < (PAIR ? NCLS : 1); ++c) acc1[r][c] = zero4;
     auto contract = [&](const u32x4 (&a)[NOP], const u32x4 v, float4_t (&ac)[NCLS]) __attribute__((always_inline)) {
         if constexpr (TWO) {
             const u32x4 u = v >> 12u;
@@ -229,7 +231,7 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
     // (pair: the same chunks of the second matrix, requested in the order they are used)
     const __amdgpu_buffer_rsrc_t wr1 =
         rsrc(gr.Wp[PAIR ? 1 : 0] + (int64_t)n0 * S, __builtin_amdgcn_readfirstlane((uint32_t)(rows_here * S)));
-    u32x4 wq[RB][CST], wq1[PAIR ? CST : 1];
+    u32x4 wq[RB][CST], wq1[PAIR ? RB : 1][PAIR ? CST : 1];
 #pragma unroll
     for (int s = 0; s < CST; ++s) {
         const int c = 4 * (s * NW + wv) + g;
@@ -239,8 +241,11 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
             wq[r][s] = __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 0);
         }
         if constexpr (PAIR) {
-            const int off = c < C ? (int)(uint32_t)(j * S + c * 16) : (int)0x80000000u;
-            wq1[s] = __builtin_amdgcn_raw_buffer_load_b128(wr1, off, 0, 0);
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                const int off = c < C ? (int)(uint32_t)((16 * r + j) * S + c * 16) : (int)0x80000000u;
+                wq1[r][s] = __builtin_amdgcn_raw_buffer_load_b128(wr1, off, 0, 0);
+            }
         }
     }
 #pragma unroll
@@ -250,7 +255,7 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
         // the weights (while s < PD) and the refills (issued at the ends of the earlier steps) of
         // the steps after s
         {
-            constexpr int NWL = CST * RB + (PAIR ? CST : 0), NX = NLD + (NORM ? 1 : 0);
+            constexpr int NWL = CST * RB * (PAIR ? 2 : 1), NX = NLD + (NORM ? 1 : 0);
             int after = 0;
             for (int u = s + 1; u < PD; ++u) after += NX;
             if (s < PD) after += NWL;
@@ -306,7 +311,10 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
         // decode and contract
 #pragma unroll
         for (int r = 0; r < RB; ++r) contract(a, wq[r][s], acc[r]);
-        if constexpr (PAIR) contract(a, wq1[s], acc1);
+        if constexpr (PAIR) {
+#pragma unroll
+            for (int r = 0; r < RB; ++r) contract(a, wq1[r][s], acc1[r]);
+        }
         // refill the slot with step s + PD once its reads are done.  (Issued after the contraction:
         // the compiler's own waits for the weight registers do not count the loads to LDS, so a
         // refill issued earlier would be waited for with them -- measured 4% slower at 11008 -> 4096,
@@ -338,9 +346,12 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
         for (int e = 0; e < 4; ++e) red[wv][4 * g + e][16 * RB] = accx[e];
     }
     if constexpr (PAIR) {
-        const float4_t t1 = merge(acc1);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) red1[wv][4 * g + e][j] = t1[e];
+        for (int r = 0; r < RB; ++r) {
+            const float4_t t1 = merge(acc1[r]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) red1[wv][4 * g + e][16 * r + j] = t1[e];
+        }
     }
     if constexpr (NORM) {
         const float q = sum_over_rows(xsq);      // lanes j, j+16, j+32, j+48 hold parts of row j
@@ -392,12 +403,14 @@ constexpr bool has_glue()
 
 // Several 16-row blocks per workgroup (RB): every activation value a wave reads feeds RB
 // blocks, so the activations are re-read from cache RB times less often.  Variants exist for
-// eight waves, without glue or with the norm, and only where the registers do not spill.
+// eight waves, without glue or with the norm, and only where the registers do not spill; the
+// pair variant takes two blocks of each matrix for tiles of up to 8 rows and 2 steps (its two
+// sets of accumulators).
 template <int FMT, int MT, int CST, int RB, int GL>
 constexpr bool has_rb()
 {
     if (RB == 1) return true;
-    if (GL & kGluePair) return false;
+    if (GL & kGluePair) return RB == 2 && MT <= 8 && CST <= 2;
     const int c = CST + ((GL & kGlueNorm) ? 1 : 0);   // the norm takes about one more step's registers
     if (RB == 2) return FMT == TRI_FMT_2BIT ? (MT == 16 ? c <= 6 : c <= 8) : (MT == 16 ? c <= 5 : c <= 6);
     // (1.6-bit tiles of 4 rows: four blocks measured 4% slower than two; of 8 rows, the
@@ -411,7 +424,10 @@ template <int FMT, int MT, int NW, int CST, int GL, int RB>
 static bool launch_gl(const uint16_t *X, const Groups &gr, int M, int K, int C, hipStream_t s, const Fusion &f)
 {
     if constexpr (has_glue<FMT, MT, NW, CST, GL>() && has_rb<FMT, MT, CST, RB, GL>()) {
-        const Groups g = RB == 1 ? gr : regroup(gr, RB);
+        Groups g = RB == 1 ? gr : regroup(gr, RB);
+        if constexpr ((GL & kGluePair) != 0) {   // (the grid covers the first matrix's blocks only)
+            for (int q = 2; q <= kMaxGroups; ++q) g.blk[q] = g.blk[1];
+        }
         const dim3 grid(g.blk[g.G], (M + 15) / 16), block(64 * NW);
         // (single-matrix variants for the plain layer only: the glue variants serve grouped launches)
         if (GL == 0 && g.G == 1)
@@ -435,8 +451,12 @@ static bool launch_cfg(const uint16_t *X, const Groups &gr, int M, int K, int C,
             if (rb >= 2 && launch_gl<FMT, MT, NW, CST, kGlueNorm, 2>(X, gr, M, K, C, s, f)) return true;
         }
         return launch_gl<FMT, MT, NW, CST, kGlueNorm, 1>(X, gr, M, K, C, s, f);
-    case kGluePair: return launch_gl<FMT, MT, NW, CST, kGluePair, 1>(X, gr, M, K, C, s, f);
-    case kGlueNorm | kGluePair: return launch_gl<FMT, MT, NW, CST, kGlueNorm | kGluePair, 1>(X, gr, M, K, C, s, f);
+    case kGluePair:
+        if (rb >= 2 && launch_gl<FMT, MT, NW, CST, kGluePair, 2>(X, gr, M, K, C, s, f)) return true;
+        return launch_gl<FMT, MT, NW, CST, kGluePair, 1>(X, gr, M, K, C, s, f);
+    case kGlueNorm | kGluePair:
+        if (rb >= 2 && launch_gl<FMT, MT, NW, CST, kGlueNorm | kGluePair, 2>(X, gr, M, K, C, s, f)) return true;
+        return launch_gl<FMT, MT, NW, CST, kGlueNorm | kGluePair, 1>(X, gr, M, K, C, s, f);
     default:
         if constexpr (NW == 8) {
             if (rb >= 4 && launch_gl<FMT, MT, NW, CST, 0, 4>(X, gr, M, K, C, s, f)) return true;
@@ -508,7 +528,10 @@ bool launch_mvm(const uint16_t *X, const Groups &gr, int M, int K, int fmt, hipS
         16 * (int64_t)C * 16 >= ((int64_t)1 << 31))
         return false;
     if (M > 16 && fu) return false;              // the block glue serves up to 16 rows
-    const int rb = (glue_bits(fu) & kGluePair) ? 1 : choose_rb(gr, M);
+    // (the pair's grid covers the first matrix only: its block count decides, at most two blocks)
+    Groups first = gr;
+    first.G = 1;
+    const int rb = (glue_bits(fu) & kGluePair) ? (choose_rb(first, M) >= 2 ? 2 : 1) : choose_rb(gr, M);
     if (fmt == TRI_FMT_2BIT) {
         if (M <= 4) return launch_mt<TRI_FMT_2BIT, 4>(X, gr, M, K, C, s, fu, rb);
         if (M <= 8) return launch_mt<TRI_FMT_2BIT, 8>(X, gr, M, K, C, s, fu, rb);

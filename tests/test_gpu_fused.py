@@ -146,6 +146,28 @@ def test_fused_silu_pair(fmt, shape):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M,K", [(5, 1000), (8, 4096), (6, 4000)])
+def test_fused_silu_pair_two_block_workgroups(fmt, M, K):
+    """Gate and up of 5150 rows: at least 160 workgroups of two 16-row blocks of each matrix, so the
+    batched kernel's pair variant takes two blocks per workgroup; the last workgroup holds a full
+    block and one of 14 rows."""
+    Ns = [5150, 5150]
+    Ws, scales, X, gain, Rs = inputs(M, K, Ns, 986)
+    Wps = [tri.pack(cuda(W), fmt) for W in Ws]
+    worst = 0.0
+    for opt in PAIRED:
+        norm = bool(opt.get("norm"))
+        gn = gain if opt.get("gain") else None
+        R = [Rs[0], None] if opt.get("res") else None
+        say("pair two blocks M=%d K=%d fmt=%d %s" % (M, K, fmt, opt["name"]))
+        Y = run_fused(X, Wps, scales, Ns, K, fmt, norm=norm, gain=gn, pair=True, Rs=R)[0]
+        what = "two-block pair M=%d K=%d fmt=%d %s" % (M, K, fmt, opt["name"])
+        worst = max(worst, check_pair(Y, X, Ws[0], scales[0], Ws[1], scales[1], norm, gn, 1e-5,
+                                      None if R is None else R[0], what))
+    say("pair two blocks M=%d K=%d fmt=%d: worst error / tolerance %.3f" % (M, K, fmt, worst))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("M", [4, 8, 16])
 def test_fused_norm_multi_block_workgroups(fmt, M):
     """Grids large enough for workgroups of several 16-row blocks (4096 + 4096 + 2000 rows): the
