@@ -74,7 +74,6 @@ __device__ __forceinline__ uint32_t digits_to_t(uint32_t w, uint32_t bias)
 }  // namespace
 
 constexpr int kBM = 128;             // rows of Y per workgroup
-constexpr int kMT = 4;               // 32-row MFMA tiles per wave
 constexpr int kBN = 512;             // columns of Y per tile (4 waves side by side, 4 MFMA tiles each)
 
 // A workgroup computes one BM x 512 tile of Y (NT = 4), one half of it, BM x 256 (NT = 2), or one
