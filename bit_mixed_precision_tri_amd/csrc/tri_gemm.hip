@@ -5,7 +5,7 @@
 // Here it is a dense contraction (the review's "high-batch" regime), so it runs as a tiled
 // fp16 MFMA GEMM (v_mfma_f32_32x32x16_f16) whose B operand is decoded from the packed
 // trits in registers -- the gfx950 counterpart of the pages' FP16 x INT2 tensor-core
-// kernel with fused dequantisation.
+// kernel with fused dequantisation and asynchronous copies.
 //
 // Tiling.  A workgroup of 4 waves computes a 128 x 512 tile of Y; wave w owns output
 // columns 128w..128w+127 (four 32-column MFMA tiles) for all 128 rows (four 32-row tiles):
@@ -13,23 +13,28 @@
 // feeds four MFMAs and every decoded B operand four.  K advances in tiles of one 32-byte
 // packed slice per weight row: 128 trits (2-bit, 8 MFMA k-steps of 16) or 160 trits (1.6-bit,
 // 10 k-steps).
-//  - B (weights): lane (h = lane/32, c = lane%32) of column tile nt loads bytes 16h..16h+15
-//    of the slice of weight row 32nt + c with one 16-byte buffer load (prefetched one K tile
-//    ahead) and turns them into exact fp16 values of t: a 2-bit digit pair of a register,
-//    moved to bits 0-1 / 16-17, is OR-ed into 1024.0 (0x6400) and 1025 is subtracted with one
-//    packed fp16 add.  1.6-bit bytes first go through a 256-entry LDS table to the 2-bit
-//    digit layout (five base-3 digits; the repeated division b'_i -> x_i that the review's
-//    referee report describes for the paper's section 3.2), two bytes per register.
-//  - Order of k: a 2-bit register pairs trits (16q+p, 16q+8+p) of its 16 and a 1.6-bit code
-//    register trits (5r+p, 5r+20+p) of a 40-trit group; the sum over k is order-free, so the
-//    activations are permuted the same way (v_perm_b32) when they are staged and no weight
-//    byte is ever reshuffled.
-//  - A (activations): each K tile of the 128 rows is loaded with buffer loads (rows past M
-//    and values past K read as zero), permuted, and written to one of two LDS buffers in
-//    k-step order ([k-step][h][8 values] per row), so an A operand is one 16-byte LDS read.
+//  - Order of k: lane half h (lane / 32) of every operand covers the K tile's values
+//    KS*8*h ... (KS k-steps), eight consecutive ones per k-step, so an A operand is one
+//    16-byte piece of an activation row as it lies in memory.
+//  - B (weights): lane (h, c = lane%32) of column tile nt loads bytes 16h..16h+15 of the slice
+//    of weight row 32nt + c with one 16-byte buffer load (prefetched one K tile ahead); for
+//    1.6-bit, a 256-entry LDS table turns each byte into its five base-3 digits as 2-bit
+//    digits (the repeated division b'_i -> x_i that the review's referee report describes for
+//    the paper's section 3.2), which are joined into the same 2-bit digit stream.  A k-step
+//    takes two bytes of the stream; each byte is copied into both 16-bit halves of a register
+//    (v_perm_b32), and two adjacent digits become an exact fp16 pair with one v_and_or_b32
+//    and one packed fp16 add (digits_pair).
+//  - A (activations): each K tile of the 128 rows is written into one of two LDS buffers by
+//    gfx950 buffer loads to LDS (16 bytes per lane, no registers and no LDS write
+//    instructions on the way; rows past M and values past K read as zero), one K tile ahead:
+//    the analogue of the asynchronous copies of the pages' kernel.  A load instruction reads
+//    64 contiguous bytes (four lanes) of each of 16 rows, and the layout in LDS keeps the 16
+//    rows that one read pass touches in 16 distinct bank groups.
 //  - Software pipeline: the 16 MFMAs of a k-step run while the A and B operands of the next
-//    k-step are read and decoded; the next K tile is loaded at the start of a tile and
-//    staged before its last k-step, where the single barrier of the tile sits.
+//    k-step are read and decoded; at the last k-step of a tile every wave waits for its share
+//    of the next tile's activations (an explicit vmcnt: the compiler does not wait for what
+//    loads to LDS write before a barrier), the single barrier of the tile follows, and the
+//    loads of the tile after next are issued into the buffer and the registers just freed.
 // Workgroups are mapped to tiles XCD by XCD: consecutive workgroups of one XCD take
 // consecutive row tiles of the same column tiles, so they share weights and activations in
 // that XCD's L2.
@@ -60,14 +65,31 @@ __device__ __forceinline__ float16_t mfma32(const u32x4 a, const u32x4 b, float1
                                                   0, 0);
 }
 
-// Exact fp16 pair (t_lo, t_hi) from the two 2-bit digits of `w` at bits 0-1 and 16-17:
-// (w & 0x00030003) | 0x64006400 is (1024 + d_lo, 1024 + d_hi), and adding (-1025, -1025)
-// leaves t = d - 1.  `bias` holds 0x64006400 in a vector register, so mask and bias fuse
-// into one v_and_or_b32 (a gfx9 VOP3 instruction takes no literal and one scalar operand).
-__device__ __forceinline__ uint32_t digits_to_t(uint32_t w, uint32_t bias)
+typedef __attribute__((address_space(3))) char *lds_ptr_t;
+
+// s_waitcnt vmcnt(N): at most N vector memory loads of this wave still outstanding (they
+// retire in issue order), the other counters not waited for
+template <int N>
+__device__ __forceinline__ void wait_vm()
 {
-    const uint32_t biased = (w & 0x00030003u) | bias;
-    const half2_t r = as_h2(biased) + as_h2(0xE401E401u);
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | (((N >> 4) & 3) << 14));
+}
+
+// Exact fp16 pair (t_a, t_a+1) from two adjacent 2-bit digits of one byte, which `d` holds in
+// both 16-bit halves (digit j at bits 2j): the low half keeps digit a in its mantissa, the high
+// half digit a + 1, each OR-ed into the power of two 2^e whose mantissa step at that position
+// is 1.0 (a = 0: 1024 + d and 256 + d; a = 2: 64 + d and 16 + d), and one packed fp16 add of
+// -(2^e + 1) leaves t = d - 1 in each half, exactly.  `bias` holds the two powers of two in a
+// vector register, so mask and bias fuse into one v_and_or_b32 (a gfx9 VOP3 instruction takes
+// no literal and one scalar operand).
+template <int A>
+__device__ __forceinline__ uint32_t digits_pair(uint32_t d, uint32_t bias)
+{
+    static_assert(A == 0 || A == 2, "digit pairs 0-1 and 2-3 of a byte");
+    constexpr uint32_t mask = A == 0 ? 0x000C0003u : 0x00C00030u;
+    constexpr uint32_t sub = A == 0 ? 0xDC04E401u : 0xCC40D410u;   // (-1025, -257) / (-65, -17)
+    const half2_t r = as_h2((d & mask) | bias) + as_h2(sub);
     return __builtin_bit_cast(uint32_t, r);
 }
 
@@ -91,15 +113,21 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t *__restrict__ X, co
     constexpr bool TWO = FMT == TRI_FMT_2BIT;
     constexpr int BK = TWO ? 128 : 160;          // trits per K tile (32 packed bytes per weight row)
     constexpr int KS = BK / 16;                  // MFMA k-steps per K tile
-    constexpr int ASTR = BK + 8;                 // LDS row stride in halves (16 bytes of padding)
-    // activation groups: the values whose weight trits share decode registers (16 for 2-bit,
-    // 40 for 1.6-bit); a thread loads whole groups, lanes walking along a row
-    constexpr int GV = TWO ? 16 : 40;            // values per group
-    constexpr int GPR = BK / GV;                 // groups per row and K tile (8 or 4)
-    constexpr int GP = GV / 8;                   // 16-byte pieces per group
-    constexpr int NG = kBMt * GPR / 256;          // groups per thread and K tile
-    constexpr int XP = NG * GP;                  // 16-byte pieces per thread and K tile
-    __shared__ uint16_t abuf[2][kBMt * ASTR];
+    constexpr int PR = BK / 8;                   // 16-byte activation pieces per row and K tile (16 or 20)
+    constexpr int NW = TWO ? 4 : 5;              // 32-bit words of 2-bit digits per lane and weight row
+    // A buffers, in 16-byte pieces: piece q of tile row r at
+    //   (r / 16) 16 PR + (q / 4) 64 + 4 (r % 16) + ((q % 4) ^ ((r % 16) / 4)),
+    // so a load instruction fills 64 consecutive positions, a block of 16 rows x 4 pieces whose
+    // rows each take 4 consecutive lanes (64 contiguous bytes of the row), and the 16 rows that
+    // one LDS read pass touches at one piece fall in 16 distinct bank groups (the XOR).  NI load
+    // instructions per wave and tile.  Two separate arrays, not one indexed by a variable: loads
+    // to LDS are waited for before LDS reads the compiler cannot prove disjoint from them, and
+    // it proves it for distinct arrays.
+    constexpr int NI = kBMt * PR / 256;
+    static_assert(kBMt * PR % 256 == 0, "whole load instructions per wave");
+    __shared__ u32x4 abuf0[kBMt * PR];
+    __shared__ u32x4 abuf1[kBMt * PR];
+    auto abuf_of = [&](int b) -> u32x4 * { return b ? abuf1 : abuf0; };
     __shared__ uint32_t lut[TWO ? 1 : 256];
 
     const int tid = threadIdx.x;
@@ -143,20 +171,35 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t *__restrict__ X, co
     const int wrow = __builtin_amdgcn_readfirstlane(min(n0, N - 1));
     const __amdgpu_buffer_rsrc_t wr = rsrc(Wp + (int64_t)wrow * S, wbytes);
     const int KT = (C + 1) / 2;                  // K tiles (two 16-byte chunks each)
+    const int KTe = (KT + 1) & ~1;               // padded to an even count (see the tile loop)
 
-    // Activations of K tile kt (tiles past the end read zeros: the k < K test and the
-    // buffer range check); group gi = q*256 + tid is group gi % GPR of row gi / GPR.
-    auto load_a = [&](int kt, u32x4 (&xa)[XP]) {
+    // The lane's offset in each of its load instructions at K tile 0 (a tile adds its first
+    // value's offset).  Rows past M lie past the buffer and read zeros; pieces past K get an
+    // offset past the buffer.  (The out-of-range offset is held in a register: as a literal it
+    // would be rebuilt before every select.)  Instruction I of a tile (the wave's i-th) fills
+    // rows 16 (I / (PR/4)) + lane / 4, pieces 4 (I % (PR/4)) + ((lane % 4) ^ (lane / 16)).
+    uint32_t oob;
+    asm volatile("v_mov_b32 %0, 0x80000000" : "=v"(oob));
+    auto piece_of = [&](int i) { return 4 * ((wv * NI + i) % (PR / 4)) + ((lane & 3) ^ (lane >> 4)); };
+    auto row_of = [&](int i) { return 16 * ((wv * NI + i) / (PR / 4)) + (lane >> 2); };
+    uint32_t xoff[NI];
+    int klim[NI];                                // the piece's values exist in tiles with k0 < klim
 #pragma unroll
-        for (int q = 0; q < NG; ++q) {
-            const int gi = q * 256 + tid;
-            const int row = gi / GPR, G = gi % GPR;
+    for (int i = 0; i < NI; ++i) {
+        const int row = row_of(i);
+        xoff[i] = (uint32_t)(row * K + 8 * piece_of(i)) * 2u;
+        klim[i] = K - 8 * piece_of(i);
+    }
+    // Activations of K tile kt into buffer `buf` (tiles past the end read zeros).  The K test
+    // is a per-lane select, not a branch: a branch would split the tile body into blocks, and
+    // the compiler then sinks the next tile's first decode below these loads.
+    auto load_a = [&](int kt, int buf) {
+        const int k0 = kt * BK;                  // wave-uniform
+        const lds_ptr_t dst = (lds_ptr_t)(abuf_of(buf) + wv * NI * 64);
 #pragma unroll
-            for (int j = 0; j < GP; ++j) {
-                const int k = kt * BK + GV * G + 8 * j;
-                const uint32_t off = (uint32_t)(row * K + k) * 2u;
-                xa[q * GP + j] = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)(k < K ? off : 0x80000000u), 0, 0);
-            }
+        for (int i = 0; i < NI; ++i) {
+            const uint32_t off = k0 < klim[i] ? xoff[i] + 2u * (uint32_t)k0 : oob;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, dst + 1024 * i, 16, (int)off, 0, 0, 0);
         }
     };
     // Weights of K tile kt (a tile past the end reads bytes that are never used, within range).
@@ -167,130 +210,110 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t *__restrict__ X, co
             wb[nt] = __builtin_amdgcn_raw_buffer_load_b128(wr, (int)off, 0, 0);
         }
     };
-    // Permute each group into the pairing of the decoded weights and store it in k-step
-    // order: the 8 values lane half hh uses at k-step s sit at 16s + 8hh of the row.
-    auto store_a = [&](int buf, const u32x4 (&xa)[XP]) {
-#pragma unroll
-        for (int q = 0; q < NG; ++q) {
-            const int gi = q * 256 + tid;
-            const int row = gi / GPR, G = gi % GPR;
-            uint32_t v[GV / 2];
-#pragma unroll
-            for (int j = 0; j < GP; ++j) {
-                v[4 * j] = xa[q * GP + j][0]; v[4 * j + 1] = xa[q * GP + j][1];
-                v[4 * j + 2] = xa[q * GP + j][2]; v[4 * j + 3] = xa[q * GP + j][3];
-            }
-            uint16_t *rowp = &abuf[buf][row * ASTR];
-            if constexpr (TWO) {
-                // group G = 4hh + qq: pairs (x_p, x_{p+8}); p = 0..3 feed k-step 2qq, p = 4..7 k-step 2qq+1
-                const int hh = G >> 2, qq = G & 3;
-                uint32_t o[8];
-#pragma unroll
-                for (int p = 0; p < 8; p += 2) {
-                    o[p] = pair_halves<0>(v[4 + p / 2], v[p / 2]);
-                    o[p + 1] = pair_halves<1>(v[4 + p / 2], v[p / 2]);
-                }
-                *reinterpret_cast<u32x4 *>(rowp + 16 * (2 * qq) + 8 * hh) = u32x4{o[0], o[1], o[2], o[3]};
-                *reinterpret_cast<u32x4 *>(rowp + 16 * (2 * qq + 1) + 8 * hh) = u32x4{o[4], o[5], o[6], o[7]};
-            } else {
-                // group G = 2hh + g5: for p = 0..4, r = 0..3: (x[5r+p], x[5r+20+p]) feed k-step 5g5+p
-                const int hh = G >> 1, g5 = G & 1;
-#pragma unroll
-                for (int p = 0; p < 5; ++p) {
-                    uint32_t o[4];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int e = 5 * r + p;   // value index in the group; partner e + 20
-                        o[r] = (e & 1) ? pair_halves<1>(v[(e >> 1) + 10], v[e >> 1])
-                                       : pair_halves<0>(v[(e >> 1) + 10], v[e >> 1]);
-                    }
-                    *reinterpret_cast<u32x4 *>(rowp + 16 * (5 * g5 + p) + 8 * hh) = u32x4{o[0], o[1], o[2], o[3]};
-                }
-            }
-        }
-    };
 
     float16_t acc[kMTt][kNT];
 #pragma unroll
     for (int mt = 0; mt < kMTt; ++mt)
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) acc[mt][nt] = float16_t{};
-    uint32_t bias;
-    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(bias));   // register-held constant (no memory access)
+    uint32_t bias01, bias23;                     // register-held constants (no memory access)
+    asm volatile("v_mov_b32 %0, 0x5C006400" : "=v"(bias01));
+    asm volatile("v_mov_b32 %0, 0x4C005400" : "=v"(bias23));
 
-    // 1.6-bit: digit codes of byte pairs (b, b + 4) of each 8-byte half of the lane's 16 bytes
-    uint32_t code[kNT][TWO ? 1 : 8];
+    // 1.6-bit: the lane's 16 bytes as a stream of 2-bit digits, 80 trits in 5 words (the digits
+    // of byte b at bits 10b ...)
+    uint32_t str[kNT][TWO ? 1 : NW];
     auto take_codes = [&](const u32x4 (&wb)[kNT]) {
         if constexpr (!TWO) {
 #pragma unroll
-            for (int nt = 0; nt < kNT; ++nt)
+            for (int nt = 0; nt < kNT; ++nt) {
+                uint32_t cd[16];
 #pragma unroll
-                for (int cc = 0; cc < 8; ++cc) {
-                    const uint32_t lo = wb[nt][2 * (cc >> 2)], hi = wb[nt][2 * (cc >> 2) + 1];
-                    const int sh = 8 * (cc & 3);
-                    code[nt][cc] = lut[(lo >> sh) & 0xFFu] | (lut[(hi >> sh) & 0xFFu] << 16);
+                for (int b = 0; b < 16; ++b) cd[b] = lut[(wb[nt][b >> 2] >> (8 * (b & 3))) & 0xFFu];
+#pragma unroll
+                for (int j = 0; j < NW; ++j) {
+                    uint32_t v = 0;
+#pragma unroll
+                    for (int b = 0; b < 16; ++b) {
+                        const int lo = 10 * b - 32 * j;
+                        if (lo >= 32 || lo + 10 <= 0) continue;
+                        v |= lo >= 0 ? cd[b] << lo : cd[b] >> -lo;
+                    }
+                    str[nt][j] = v;
                 }
+            }
         }
     };
-    // B operand of k-step s, column tile nt (2-bit: from the packed words; 1.6-bit: from the codes)
+    // B operand of k-step s, column tile nt: trits 8s ... 8s+7 of the lane's, bytes 2s and
+    // 2s + 1 of its digit stream (2-bit: the packed words themselves)
     auto decode = [&](const u32x4 (&wb)[kNT], int s, int nt) {
+        uint32_t w;
+        if constexpr (TWO) w = wb[nt][s >> 1];
+        else w = str[nt][s >> 1];
         u32x4 b;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            if constexpr (TWO)
-                b[r] = digits_to_t(wb[nt][s >> 1] >> (2 * (4 * (s & 1) + r)), bias);
-            else
-                b[r] = digits_to_t(code[nt][4 * (s / 5) + r] >> (2 * (s % 5)), bias);
+        for (int e = 0; e < 2; ++e) {
+            const uint32_t sel = (uint32_t)(2 * (s & 1) + e) * 0x00010001u;   // the byte into both halves
+            const uint32_t d = perm(w, w, sel);
+            b[2 * e] = digits_pair<0>(d, bias01);
+            b[2 * e + 1] = digits_pair<2>(d, bias23);
         }
         return b;
     };
 
-    // Two weight register sets alternate between K tiles (the loop below is unrolled by two so
-    // the alternation costs no copies): a tile decodes from one while the next tile's words
-    // arrive in the other.  The activations of tile kt + 2 are loaded right after tile kt + 1's
-    // are staged, so every load has about one K tile of MFMA work to arrive.
-    u32x4 xa[XP];
+    // Loads in flight: the activations and weights of the next tile, issued a tile ahead,
+    // activations first (the scheduling barriers keep that order: the waits below count on
+    // it).  Tiles 0 and 1 are issued before the loop.
     u32x4 w0[kNT], w1[kNT];
-    // (loads are issued in the loop's order -- activations, then weights -- so the wait
-    // counts the compiler derives at the loop entry match those of the loop itself)
-    load_a(0, xa);
-    load_b(0, w0);
-    store_a(0, xa);
+    load_a(0, 0);
+    load_a(1, 1);
     __builtin_amdgcn_sched_barrier(0);
-    load_a(1, xa);
+    load_b(0, w0);
     load_b(1, w1);
-    __syncthreads();                             // tile 0's activations and the byte table
+    wait_vm<NI + 2 * kNT>();                     // tile 0's activations
+    __syncthreads();                             // every wave's share of them, and the byte table
     take_codes(w0);
-    const int aoff = c * ASTR + 8 * h;
+    // lane (h, c) reads row 32mt + c, piece KS h + s at step s
+    uint32_t aadr[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        const int q = KS * h + s, r = c & 15;
+        aadr[s] = 16u * (uint32_t)((c >> 4) * 16 * PR + (q >> 2) * 64 + 4 * r + ((q & 3) ^ (r >> 2)));
+    }
+    auto read_a = [&](int buf, int s, int mt) {
+        return *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(abuf_of(buf)) + aadr[s] +
+                                                16 * 32 * PR * mt);
+    };
     u32x4 afr[kMTt], bop[kNT];
 #pragma unroll
-    for (int mt = 0; mt < kMTt; ++mt) afr[mt] = *reinterpret_cast<const u32x4 *>(&abuf[0][aoff + 32 * mt * ASTR]);
+    for (int mt = 0; mt < kMTt; ++mt) afr[mt] = read_a(0, 0, mt);
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) bop[nt] = decode(w0, 0, nt);
 
     // One K tile: wc holds its weights, wx those of the next tile.  MORE (compile-time, so the
     // tile body has no branches) says whether a next tile exists.
-    auto tile = [&](int kt, auto more_tag, u32x4 (&wc)[kNT], u32x4 (&wx)[kNT]) __attribute__((always_inline)) {
+    auto tile = [&](int kt, auto more_tag, auto buf_tag, u32x4 (&wc)[kNT], u32x4 (&wx)[kNT]) __attribute__((always_inline)) {
         constexpr bool MORE = decltype(more_tag)::value;
-        const int buf = kt & 1;
-        const uint16_t *acur = &abuf[buf][aoff];
-        const uint16_t *anext = &abuf[buf ^ 1][aoff];
+        constexpr int buf = decltype(buf_tag)::value;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            // every wave has stored its share of the next tile (step KS - 2) and read its
-            // last operands of this one: the next tile's buffer may be read from here on
-            if (MORE && s == KS - 1) __syncthreads();
+            if (MORE && s == KS - 1) {
+                // this wave's share of the next tile's activations is in (only the weight
+                // loads issued after it may still be in flight) and its reads of this tile are
+                // done; after the barrier, every wave's are
+                __builtin_amdgcn_s_waitcnt(0x0070 | kNT);   // vmcnt(kNT) lgkmcnt(0)
+                __syncthreads();
+            }
             u32x4 an[kMTt], bn[kNT];
             if (s + 1 < KS) {
 #pragma unroll
-                for (int mt = 0; mt < kMTt; ++mt)
-                    an[mt] = *reinterpret_cast<const u32x4 *>(acur + 32 * mt * ASTR + 16 * (s + 1));
+                for (int mt = 0; mt < kMTt; ++mt) an[mt] = read_a(buf, s + 1, mt);
 #pragma unroll
                 for (int nt = 0; nt < kNT; ++nt) bn[nt] = decode(wc, s + 1, nt);
             } else if (MORE) {
 #pragma unroll
-                for (int mt = 0; mt < kMTt; ++mt) an[mt] = *reinterpret_cast<const u32x4 *>(anext + 32 * mt * ASTR);
-                take_codes(wx);                  // the last decode of this tile's codes was at step KS - 2
+                for (int mt = 0; mt < kMTt; ++mt) an[mt] = read_a(buf ^ 1, 0, mt);
+                take_codes(wx);                  // the last decode of this tile's stream was at step KS - 2
 #pragma unroll
                 for (int nt = 0; nt < kNT; ++nt) bn[nt] = decode(wx, 0, nt);
             }
@@ -298,7 +321,6 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t *__restrict__ X, co
             for (int mt = 0; mt < kMTt; ++mt)
 #pragma unroll
                 for (int nt = 0; nt < kNT; ++nt) acc[mt][nt] = mfma32(afr[mt], bop[nt], acc[mt][nt]);
-            if (MORE && s == KS - 2) store_a(buf ^ 1, xa);
             // interleave: each MFMA is followed by a share of the next step's decode and reads
 #pragma unroll
             for (int i = 0; i < kMTt * kNT; ++i) {
@@ -307,8 +329,12 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t *__restrict__ X, co
                 if (i % 4 == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
             }
             __builtin_amdgcn_sched_barrier(0);
-            if (MORE && s == KS - 2) load_a(kt + 2, xa);   // past the last tile: zeros, never stored
-            if (MORE && s == KS - 1) load_b(kt + 2, wc);   // wc's last decode was at step KS - 2
+            if (MORE && s == KS - 1) {
+                // this tile's buffer and weight registers are free: the tile after next
+                load_a(kt + 2, buf);
+                __builtin_amdgcn_sched_barrier(0);
+                load_b(kt + 2, wc);
+            }
             if (s + 1 < KS || MORE) {
 #pragma unroll
                 for (int mt = 0; mt < kMTt; ++mt) afr[mt] = an[mt];
@@ -319,13 +345,13 @@ __global__ __launch_bounds__(256) void k_gemm(const uint16_t *__restrict__ X, co
     };
     // An even number of tiles keeps a single code path: an odd count gets one more tile past
     // the end, whose activations read as zero, so it adds exact zeros.
-    const int KTe = (KT + 1) & ~1;
     for (int kt = 0; kt + 2 < KTe; kt += 2) {
-        tile(kt, std::true_type{}, w0, w1);
-        tile(kt + 1, std::true_type{}, w1, w0);
+        tile(kt, std::true_type{}, std::integral_constant<int, 0>{}, w0, w1);
+        tile(kt + 1, std::true_type{}, std::integral_constant<int, 1>{}, w1, w0);
     }
-    tile(KTe - 2, std::true_type{}, w0, w1);
-    tile(KTe - 1, std::false_type{}, w1, w0);
+    tile(KTe - 2, std::true_type{}, std::integral_constant<int, 0>{}, w0, w1);
+    tile(KTe - 1, std::false_type{}, std::integral_constant<int, 1>{}, w1, w0);
+    wait_vm<0>();                                // (the last tile's loads to LDS, past the end, are in)
 
     // epilogue: lane (h, c) holds rows 32mt + 8i + 4h + v of column 32nt + c
 #pragma unroll
