@@ -198,26 +198,30 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
             for (int e = 0; e < 4; ++e) xsum[r] = dot2(xv[r][i][e], 0x3C003C00u, xsum[r]);   // (x_lo, x_hi) . (1, 1)
     }
     if constexpr (TWO) {
-        // lanes 2v, 2v+1 of a chunk's eight hold x[16v .. 16v+7] and x[16v+8 .. 16v+15]: they swap
-        // pieces (DPP quad_perm [1,0,3,2]); the even lane forms positions 0..3, the odd one 4..7
+        // lanes 2v, 2v+1 of a chunk's eight hold x[16v .. 16v+7] and x[16v+8 .. 16v+15]; the even
+        // lane forms positions 0..3 from registers 0, 1 of both pieces, the odd one 4..7 from
+        // registers 2, 3.  Each lane keeps the two registers it needs of its own piece and sends the
+        // two its partner needs (DPP quad_perm [1,0,3,2]); one byte permute per A operand then puts
+        // the value of trit 16v+p in the low half (the even lane's own, the odd lane's received)
         const bool odd = lane & 1;
         const int vv = (lane & 7) >> 1;
+        const uint32_t sel0 = odd ? 0x05040100u : 0x01000504u;   // low halves: (received, own) / (own, received)
+        const uint32_t sel1 = odd ? 0x07060302u : 0x03020706u;   // high halves, the same way
 #pragma unroll
         for (int r = 0; r < MR; ++r)
 #pragma unroll
             for (int i = 0; i < NLD; ++i) {
                 const int l = (64 * i + lane) / PIECES;
-                u32x4 other;
+                const u32x4 m = xv[r][i];
+                uint32_t own[2], rcv[2];
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    other[e] = (uint32_t)__builtin_amdgcn_mov_dpp((int)xv[r][i][e], 0xB1, 0xF, 0xF, false);
-                const u32x4 lo = odd ? other : xv[r][i];
-                const u32x4 hi = odd ? xv[r][i] : other;
+                for (int h = 0; h < 2; ++h) {
+                    own[h] = odd ? m[2 + h] : m[h];
+                    rcv[h] = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? m[h] : m[2 + h]), 0xB1, 0xF, 0xF, false);
+                }
 #pragma unroll
                 for (int pp = 0; pp < 4; ++pp) {
-                    const uint32_t dlo = odd ? lo[2 + pp / 2] : lo[pp / 2];
-                    const uint32_t dhi = odd ? hi[2 + pp / 2] : hi[pp / 2];
-                    const uint32_t v = (pp & 1) ? pair_halves<1>(dhi, dlo) : pair_halves<0>(dhi, dlo);
+                    const uint32_t v = perm(own[pp / 2], rcv[pp / 2], (pp & 1) ? sel1 : sel0);
                     if (l < NCH) reinterpret_cast<uint32_t *>(&xa[wv][l][r][pp + (odd ? 4 : 0)])[vv] = v;
                 }
             }
@@ -319,8 +323,9 @@ __global__ __launch_bounds__(64 * NW) void k_mv1(const uint16_t *__restrict__ X,
 #pragma unroll
         for (int s = 0; s < CST; ++s) {
             // wave-uniform: no chunk of this step is live (the block loop contracts such steps,
-            // whose activations are zero: a skipped step would leave its loads pending)
-            if (!PS && 4 * (s * NW + wv) >= C) break;
+            // whose activations are zero: a skipped step would leave its loads pending; step 0
+            // always runs, so every accumulator's first MFMA takes a literal zero)
+            if (!PS && s > 0 && 4 * (s * NW + wv) >= C) break;
             const u32x4 *asrc;                   // A row j: activation row j % MR
             if constexpr (TWO) asrc = &xa[wv][4 * s + g][j % MR][0];
             else asrc = &xb[wv][j % MR][(4 * s + g) * NOP];

@@ -250,7 +250,10 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
     }
 #pragma unroll
     for (int s = 0; s < CST; ++s) {
-        if (4 * (s * NW + wv) >= C) break;       // wave-uniform: no chunk of this step is live
+        // wave-uniform: no chunk of this step is live.  (Step 0 always runs -- a wave without a
+        // live chunk contracts zeros -- so every accumulator's first MFMA takes a literal zero
+        // instead of registers zeroed ahead of the loop.)
+        if (s > 0 && 4 * (s * NW + wv) >= C) break;
         // wait for this step's pieces: loads issued after them are the later prefetched steps,
         // the weights (while s < PD) and the refills (issued at the ends of the earlier steps) of
         // the steps after s
