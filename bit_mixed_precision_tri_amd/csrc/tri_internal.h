@@ -93,16 +93,27 @@ inline Groups regroup(const Groups &gr, int RB)
     return g;
 }
 
-// Blocks per workgroup: the largest RB whose grid (over every 16-row slice of the activations)
-// still gives 5/8 of a workgroup per CU.  Fewer, fuller workgroups win down to about that
-// point (measured at M = 4..64 on 4096 -> 11008, 11008 -> 4096 and 4096 -> 4096: 172
-// four-block workgroups beat 688 one-block ones by 15-25%; 128 lose to 256).
-inline int choose_rb(const Groups &gr, int M)
+// Blocks per workgroup (1..4).  A workgroup costs about one block's work on top of its blocks
+// (it stages the activations of the whole K range once: measured at M = 4..64 on 4096 -> 11008,
+// 11008 -> 4096 and 4096 -> 4096, 172 four-block workgroups beat 688 one-block ones by 15-25%,
+// and 128 two-block ones lose to 256 one-block ones), and the grid runs in rounds of one
+// workgroup per CU, so the busiest CU costs rounds * (1 + RB).  The cheapest RB is taken, the
+// larger on a tie (fewer activation re-reads): 688 blocks take three per workgroup (230
+// workgroups, one round), 256 blocks one.  At most max_rb blocks.
+inline int choose_rb(const Groups &gr, int M, int max_rb = 4)
 {
-    const int64_t slices = (M + 15) / 16;
-    for (int rb = 4; rb > 1; rb /= 2)
-        if (regroup(gr, rb).blk[gr.G] * slices >= cu_count() * 5 / 8) return rb;
-    return 1;
+    const int64_t slices = (M + 15) / 16, cus = cu_count();
+    int best = 1;
+    int64_t best_cost = -1;
+    for (int rb = max_rb; rb >= 1; --rb) {
+        const int64_t w = (int64_t)regroup(gr, rb).blk[gr.G] * slices;
+        const int64_t cost = (w + cus - 1) / cus * (1 + rb);
+        if (best_cost < 0 || cost < best_cost) {
+            best = rb;
+            best_cost = cost;
+        }
+    }
+    return best;
 }
 
 // Glue of a decode block folded around a (grouped) layer in the small-M kernels.  The

@@ -87,7 +87,7 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
 {
     constexpr bool NORM = (GL & kGlueNorm) != 0;
     constexpr bool PAIR = (GL & kGluePair) != 0;
-    static_assert(!PAIR || RB <= 2, "the pair variant owns one or two 16-row blocks of each matrix per workgroup");
+    static_assert(!PAIR || RB <= 3, "the pair variant owns one to three 16-row blocks of each matrix per workgroup");
     const GroupSel grp = select_group<ONE>(gr, fu, (int)blockIdx.x);
     const uint8_t *__restrict__ Wp = grp.Wp;
     const float scale = grp.scale;
@@ -406,19 +406,19 @@ constexpr bool has_glue()
 
 // Several 16-row blocks per workgroup (RB): every activation value a wave reads feeds RB
 // blocks, so the activations are re-read from cache RB times less often.  Variants exist for
-// eight waves, without glue or with the norm, and only where the registers do not spill; the
-// pair variant takes two blocks of each matrix for tiles of up to 8 rows and 2 steps (its two
-// sets of accumulators).
+// eight waves, without glue or with the norm, and only where the registers do not spill (three
+// blocks wherever four exist); the pair variant takes two or three blocks of each matrix for
+// tiles of up to 8 rows and 2 steps (its two sets of accumulators).
 template <int FMT, int MT, int CST, int RB, int GL>
 constexpr bool has_rb()
 {
     if (RB == 1) return true;
-    if (GL & kGluePair) return RB == 2 && MT <= 8 && CST <= 2;
+    if (GL & kGluePair) return (RB == 2 || RB == 3) && MT <= 8 && CST <= 2;
     const int c = CST + ((GL & kGlueNorm) ? 1 : 0);   // the norm takes about one more step's registers
     if (RB == 2) return FMT == TRI_FMT_2BIT ? (MT == 16 ? c <= 6 : c <= 8) : (MT == 16 ? c <= 5 : c <= 6);
     // (1.6-bit tiles of 4 rows: four blocks measured 4% slower than two; of 8 rows, the
     // quotient accumulators take one step's registers)
-    if (RB == 4)
+    if (RB == 3 || RB == 4)
         return MT == 16 ? c <= 3 : MT == 8 ? c <= (FMT == TRI_FMT_2BIT ? 4 : 3) : (FMT == TRI_FMT_2BIT && c <= 5);
     return false;
 }
@@ -451,18 +451,22 @@ static bool launch_cfg(const uint16_t *X, const Groups &gr, int M, int K, int C,
     case kGlueNorm:
         if constexpr (NW == 8) {                 // the largest RB up to rb that has a variant
             if (rb >= 4 && launch_gl<FMT, MT, NW, CST, kGlueNorm, 4>(X, gr, M, K, C, s, f)) return true;
+            if (rb >= 3 && launch_gl<FMT, MT, NW, CST, kGlueNorm, 3>(X, gr, M, K, C, s, f)) return true;
             if (rb >= 2 && launch_gl<FMT, MT, NW, CST, kGlueNorm, 2>(X, gr, M, K, C, s, f)) return true;
         }
         return launch_gl<FMT, MT, NW, CST, kGlueNorm, 1>(X, gr, M, K, C, s, f);
     case kGluePair:
+        if (rb >= 3 && launch_gl<FMT, MT, NW, CST, kGluePair, 3>(X, gr, M, K, C, s, f)) return true;
         if (rb >= 2 && launch_gl<FMT, MT, NW, CST, kGluePair, 2>(X, gr, M, K, C, s, f)) return true;
         return launch_gl<FMT, MT, NW, CST, kGluePair, 1>(X, gr, M, K, C, s, f);
     case kGlueNorm | kGluePair:
+        if (rb >= 3 && launch_gl<FMT, MT, NW, CST, kGlueNorm | kGluePair, 3>(X, gr, M, K, C, s, f)) return true;
         if (rb >= 2 && launch_gl<FMT, MT, NW, CST, kGlueNorm | kGluePair, 2>(X, gr, M, K, C, s, f)) return true;
         return launch_gl<FMT, MT, NW, CST, kGlueNorm | kGluePair, 1>(X, gr, M, K, C, s, f);
     default:
         if constexpr (NW == 8) {
             if (rb >= 4 && launch_gl<FMT, MT, NW, CST, 0, 4>(X, gr, M, K, C, s, f)) return true;
+            if (rb >= 3 && launch_gl<FMT, MT, NW, CST, 0, 3>(X, gr, M, K, C, s, f)) return true;
             if (rb >= 2 && launch_gl<FMT, MT, NW, CST, 0, 2>(X, gr, M, K, C, s, f)) return true;
         }
         return launch_gl<FMT, MT, NW, CST, 0, 1>(X, gr, M, K, C, s, f);
@@ -531,10 +535,10 @@ bool launch_mvm(const uint16_t *X, const Groups &gr, int M, int K, int fmt, hipS
         16 * (int64_t)C * 16 >= ((int64_t)1 << 31))
         return false;
     if (M > 16 && fu) return false;              // the block glue serves up to 16 rows
-    // (the pair's grid covers the first matrix only: its block count decides, at most two blocks)
+    // (the pair's grid covers the first matrix only: its block count decides, at most three blocks)
     Groups first = gr;
     first.G = 1;
-    const int rb = (glue_bits(fu) & kGluePair) ? (choose_rb(first, M) >= 2 ? 2 : 1) : choose_rb(gr, M);
+    const int rb = (glue_bits(fu) & kGluePair) ? choose_rb(first, M, 3) : choose_rb(gr, M);
     if (fmt == TRI_FMT_2BIT) {
         if (M <= 4) return launch_mt<TRI_FMT_2BIT, 4>(X, gr, M, K, C, s, fu, rb);
         if (M <= 8) return launch_mt<TRI_FMT_2BIT, 8>(X, gr, M, K, C, s, fu, rb);
