@@ -493,17 +493,25 @@ static bool launch_gl(const uint16_t *X, const Groups &gr, int M, int K, int C, 
 // at M = 1) and loses both below about 200 (4096 -> 11008: 5.03 -> 5.24 us) and past one per CU,
 // where the last ones run alone (2 x 11008 grouped, 344: 7.01 -> 8.50 us).  At four rows the
 // activation traffic weighs more and it wins from about 160 on (4096 -> 11008 at M = 4: 6.98 ->
-// 5.89 us).  Two blocks lost wherever four did not win, so they are not used.
+// 5.89 us).  Two blocks lost wherever four did not win, so they are not used.  At four rows three
+// blocks are taken where they cost less by rounds x (1 + blocks) of one workgroup per CU (688
+// blocks: 230 workgroups in one round instead of 172; 4096 -> 11008 5.99 -> 5.86 us); at one row
+// they lose like four (4096 -> 11008: 4.66 -> 5.02 us).  Returns 1, 3 or 4.
 template <int FMT, int NW, int CST, int MR>
-static bool wide_rb(const Groups &gr, const Fusion *fu)
+static int wide_rb(const Groups &gr, const Fusion *fu)
 {
     if constexpr (FMT != TRI_FMT_2BIT || NW != 8 || (MR == 2 && CST > 6)) {
-        return false;
+        return 1;
     } else {
-        const int w = regroup(gr, 4).blk[gr.G];
-        if (glue_bits(fu)) return false;
-        if constexpr (MR == 4) return w >= 160;
-        else return w >= (MR == 1 ? 200 : 160) && w <= cu_count();
+        if (glue_bits(fu)) return 1;
+        const int64_t cus = cu_count();
+        const int w4 = regroup(gr, 4).blk[gr.G], w3 = regroup(gr, 3).blk[gr.G];
+        if constexpr (MR == 4) {                 // (rounds of one workgroup per CU, each costing about 1 + RB blocks)
+            if (w4 < 160) return 1;
+            return (w3 + cus - 1) / cus * 4 < (w4 + cus - 1) / cus * 5 ? 3 : 4;
+        } else {
+            return w4 >= (MR == 1 ? 200 : 160) && w4 <= cus ? 4 : 1;
+        }
     }
 }
 
@@ -511,13 +519,15 @@ template <int FMT, int NW, int CST, int MR>
 static bool launch_cfg(const uint16_t *X, const Groups &gr, int M, int K, int C, hipStream_t s, const Fusion *fu)
 {
     const Fusion f = fu ? *fu : Fusion{};
-    const bool rb4 = wide_rb<FMT, NW, CST, MR>(gr, fu);
+    const int rbw = wide_rb<FMT, NW, CST, MR>(gr, fu);
     if constexpr (MR > 1) {                      // (no glue but the residual)
         if constexpr (FMT == TRI_FMT_2BIT && NW == 8 && (MR == 4 || CST <= 6)) {
-            // (a tall matrix: the block loop before four-block workgroups)
-            if (rb4 && !launch_loop<FMT, NW, CST, MR>(X, gr, M, K, C, s, f))
-                return launch_gl<FMT, NW, CST, 0, MR, 4>(X, gr, M, K, C, s, f);
-            if (rb4) return true;
+            // (a tall matrix: the block loop before several-block workgroups)
+            if (rbw > 1 && launch_loop<FMT, NW, CST, MR>(X, gr, M, K, C, s, f)) return true;
+            if (rbw == 4) return launch_gl<FMT, NW, CST, 0, MR, 4>(X, gr, M, K, C, s, f);
+            if constexpr (MR == 4) {             // (three blocks: four rows only)
+                if (rbw == 3) return launch_gl<FMT, NW, CST, 0, MR, 3>(X, gr, M, K, C, s, f);
+            }
         }
         return launch_gl<FMT, NW, CST, 0, MR, 1>(X, gr, M, K, C, s, f);
     } else {
@@ -533,7 +543,7 @@ static bool launch_cfg(const uint16_t *X, const Groups &gr, int M, int K, int C,
             if (gl & kGlueNorm) return launch_gl<FMT, NW, CST, kGlueNorm, 1, 1>(X, gr, M, K, C, s, f);
         }
         if constexpr (FMT == TRI_FMT_2BIT && NW == 8) {
-            if (rb4) return launch_gl<FMT, NW, CST, 0, 1, 4>(X, gr, M, K, C, s, f);
+            if (rbw == 4) return launch_gl<FMT, NW, CST, 0, 1, 4>(X, gr, M, K, C, s, f);
         }
         return launch_gl<FMT, NW, CST, 0, 1, 1>(X, gr, M, K, C, s, f);
     }
