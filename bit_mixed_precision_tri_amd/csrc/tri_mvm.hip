@@ -416,8 +416,9 @@ constexpr bool has_rb()
     if (GL & kGluePair) return (RB == 2 || RB == 3) && MT <= 8 && CST <= 2;
     const int c = CST + ((GL & kGlueNorm) ? 1 : 0);   // the norm takes about one more step's registers
     if (RB == 2) return FMT == TRI_FMT_2BIT ? (MT == 16 ? c <= 6 : c <= 8) : (MT == 16 ? c <= 5 : c <= 6);
-    // (1.6-bit tiles of 4 rows: four blocks measured 4% slower than two; of 8 rows, the
-    // quotient accumulators take one step's registers)
+    // (1.6-bit tiles of 4 rows: four blocks measured 4% slower than two, three are tried; of 8
+    // rows, the quotient accumulators take one step's registers)
+    if (RB == 3 && MT == 4 && FMT == TRI_FMT_1P6BIT) return c <= 4;   // (its digit sums: few accumulators)
     if (RB == 3 || RB == 4)
         return MT == 16 ? c <= 3 : MT == 8 ? c <= (FMT == TRI_FMT_2BIT ? 4 : 3) : (FMT == TRI_FMT_2BIT && c <= 5);
     return false;
