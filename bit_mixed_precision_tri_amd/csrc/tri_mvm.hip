@@ -498,6 +498,11 @@ static bool launch_mt(const uint16_t *X, const Groups &gr, int M, int K, int C, 
         }
     }
     const int cst8 = (C + 31) / 32;              // chunk-steps with 8 waves (4 chunks per step and wave)
+    // (wide: sixteen waves of three steps, decided per matrix by wide16 below)
+    if constexpr (FMT == TRI_FMT_2BIT && MT == 8) {
+        if (rb == 0) return launch_cfg<FMT, MT, 16, 3>(X, gr, M, K, C, s, fu, 1);
+    }
+    if (rb == 0) return false;
     switch (cst8) {
     case 1: return launch_cfg<FMT, MT, 8, 1>(X, gr, M, K, C, s, fu, rb);
     case 2: return launch_cfg<FMT, MT, 8, 2>(X, gr, M, K, C, s, fu, rb);
@@ -526,6 +531,21 @@ static bool launch_mt(const uint16_t *X, const Groups &gr, int M, int K, int C, 
     return false;                                // longer rows: the streaming small-M kernel
 }
 
+// Sixteen waves of three steps for 2-bit tiles of 5..8 rows whose rows take five or six
+// eight-wave steps (8192 < K <= 12288), where the matrix alone would run one block per workgroup
+// and no glue but the residual applies: 11008 -> 4096 at M = 8 7.76 -> 7.33 us (sixteen-row tiles
+// gain nothing).  The wave count changes the order of the sums, so the choice is made per
+// matrix: a group whose matrices all qualify runs as one such launch, a mixed group as one
+// launch per matrix, and every output stays bitwise equal to a single launch of its matrix.
+static bool wide16(const Groups &gr, int g, int M, int C, int fmt, const Fusion *fu)
+{
+    if (fmt != TRI_FMT_2BIT || M < 5 || M > 8 || glue_bits(fu)) return false;
+    const int cst8 = (C + 31) / 32;
+    if (cst8 < 5 || cst8 > 6) return false;
+    const Groups one = make_groups(1, &gr.Wp[g], &gr.scale[g], &gr.N[g], &gr.Y[g]);
+    return choose_rb(one, M) == 1;
+}
+
 bool launch_mvm(const uint16_t *X, const Groups &gr, int M, int K, int fmt, hipStream_t s, const Fusion *fu)
 {
     const int C = (int)(row_bytes(K, fmt) / 16);
@@ -536,6 +556,19 @@ bool launch_mvm(const uint16_t *X, const Groups &gr, int M, int K, int fmt, hipS
         16 * (int64_t)C * 16 >= ((int64_t)1 << 31))
         return false;
     if (M > 16 && fu) return false;              // the block glue serves up to 16 rows
+    int n16 = 0;
+    for (int g = 0; g < gr.G; ++g) n16 += wide16(gr, g, M, C, fmt, fu);
+    if (n16 == gr.G) return launch_mt<TRI_FMT_2BIT, 8>(X, gr, M, K, C, s, fu, 0);
+    if (n16 > 0) {                               // (a mixed group: one launch per matrix)
+        for (int g = 0; g < gr.G; ++g) {
+            const Groups one = make_groups(1, &gr.Wp[g], &gr.scale[g], &gr.N[g], &gr.Y[g]);
+            Fusion f1 = fu ? *fu : Fusion{};
+            f1.res[0] = f1.res[g];
+            for (int q = 1; q < kMaxGroups; ++q) f1.res[q] = nullptr;
+            if (!launch_mvm(X, one, M, K, fmt, s, fu ? &f1 : nullptr)) return false;
+        }
+        return true;
+    }
     // (the pair's grid covers the first matrix only: its block count decides, at most three blocks)
     Groups first = gr;
     first.G = 1;
