@@ -23,8 +23,9 @@
 // (5q+p, 5q+40+p)).  The waves' partial tiles are added in LDS in a fixed order (no atomics).
 //
 // Block glue.  Every variant adds an optional residual to the fp32 results before rounding.
-// Norm variant (GL & kGlueNorm): each lane adds the squares of its row's values and multiplies
-// them by the norm gain (rounded to fp16), which is loaded into the same slot behind the
+// Norm variant (GL & kGlueNorm): the sums of squares of the rows are the diagonal of the Gram
+// matrix of the raw activations, formed on the matrix cores; each lane then multiplies its row's
+// values by the norm gain (rounded to fp16), which is loaded into the same slot behind the
 // activations; the 1/rms factor of each row scales its results.  Pair variant
 // (GL & kGluePair): the workgroup also reads the same 16 rows of a second matrix, contracts
 // them with the same A operands, and writes fp16(silu(y0) * y1) as its only output.
@@ -218,7 +219,10 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
         }
     };
     float4_t accx = zero4;                       // sum_k X[m][k] in every column of the tile
-    float xsq = 0.f;                             // norm: sum of x^2 over this lane's values of row j
+    // norm: the Gram matrix D = X X^T of this wave's raw activations on the matrix cores (lane (g, j)
+    // supplies row j's values of chunk g as both its A and its B operand), whose diagonal D[j][j] is
+    // row j's sum of squares over the wave's chunks
+    float4_t accq = {0.f, 0.f, 0.f, 0.f};
     // the activations of PD steps are in flight at once.  The first PD steps' activations are
     // requested before the weights: the load counter is in order, so the first steps'
     // permutation overlaps the weight stream instead of waiting behind it
@@ -277,7 +281,10 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
         }
         if constexpr (NORM) {
 #pragma unroll
-            for (int q = 0; q < XH / 2; ++q) xsq = dot2(x32[q], x32[q], xsq);
+            for (int q = 0; q < XH / 8; ++q) {
+                const u32x4 xq = {x32[4 * q], x32[4 * q + 1], x32[4 * q + 2], x32[4 * q + 3]};
+                accq = mfma(xq, xq, accq);
+            }
             if (fu.gain) {
 #pragma unroll
                 for (int q = 0; q < XH / 8; ++q) {
@@ -356,9 +363,8 @@ __global__ __launch_bounds__(64 * NW) void k_mvm(const uint16_t *__restrict__ X,
             for (int e = 0; e < 4; ++e) red1[wv][4 * g + e][16 * r + j] = t1[e];
         }
     }
-    if constexpr (NORM) {
-        const float q = sum_over_rows(xsq);      // lanes j, j+16, j+32, j+48 hold parts of row j
-        if (g == 0) red[wv][j][16 * RB + 1] = q;
+    if constexpr (NORM) {                        // (D[j][j] is element j % 4 of lane (j / 4, j))
+        if (g == (j >> 2)) red[wv][j][16 * RB + 1] = accq[j & 3];
     }
     __syncthreads();
     // thread (m, jj): output Y[m][n0 + jj], waves added in a fixed order
