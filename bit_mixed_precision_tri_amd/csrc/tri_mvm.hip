@@ -504,11 +504,6 @@ static bool launch_mt(const uint16_t *X, const Groups &gr, int M, int K, int C, 
         }
     }
     const int cst8 = (C + 31) / 32;              // chunk-steps with 8 waves (4 chunks per step and wave)
-    // (wide: sixteen waves of three steps, decided per matrix by wide16 below)
-    if constexpr (FMT == TRI_FMT_2BIT && MT == 8) {
-        if (rb == 0) return launch_cfg<FMT, MT, 16, 3>(X, gr, M, K, C, s, fu, 1);
-    }
-    if (rb == 0) return false;
     switch (cst8) {
     case 1: return launch_cfg<FMT, MT, 8, 1>(X, gr, M, K, C, s, fu, rb);
     case 2: return launch_cfg<FMT, MT, 8, 2>(X, gr, M, K, C, s, fu, rb);
@@ -564,7 +559,7 @@ bool launch_mvm(const uint16_t *X, const Groups &gr, int M, int K, int fmt, hipS
     if (M > 16 && fu) return false;              // the block glue serves up to 16 rows
     int n16 = 0;
     for (int g = 0; g < gr.G; ++g) n16 += wide16(gr, g, M, C, fmt, fu);
-    if (n16 == gr.G) return launch_mt<TRI_FMT_2BIT, 8>(X, gr, M, K, C, s, fu, 0);
+    if (n16 == gr.G) return launch_cfg<TRI_FMT_2BIT, 8, 16, 3>(X, gr, M, K, C, s, fu, 1);
     if (n16 > 0) {                               // (a mixed group: one launch per matrix)
         for (int g = 0; g < gr.G; ++g) {
             const Groups one = make_groups(1, &gr.Wp[g], &gr.scale[g], &gr.N[g], &gr.Y[g]);
