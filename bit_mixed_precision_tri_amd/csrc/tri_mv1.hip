@@ -594,6 +594,13 @@ static bool launch_fmt(const uint16_t *X, const Groups &gr, int M, int K, int C,
             }
         }
     }
+    // The other 2-bit one-row matrices with rows of five or six eight-wave steps (8192 < K <= 12288):
+    // twelve waves of four steps, three waves per SIMD instead of two (11008 -> 4096: 4.99 -> 4.88 us;
+    // sixteen waves of three measured equal to eight).  The choice depends on the matrix alone, so
+    // single, grouped and residual launches of it take the same kernel.
+    if constexpr (FMT == TRI_FMT_2BIT && MR == 1) {
+        if (!glue_bits(fu) && (cst8 == 5 || cst8 == 6)) return launch_cfg<FMT, 12, 4, 1>(X, gr, M, K, C, s, fu);
+    }
     switch (cst8) {
     case 1: return launch_cfg<FMT, 8, 1, MR>(X, gr, M, K, C, s, fu);
     case 2: return launch_cfg<FMT, 8, 2, MR>(X, gr, M, K, C, s, fu);
