@@ -498,3 +498,24 @@ def test_grouped_wide_rows_same_as_single(M, K, Ns):
         Yh = host(Y)
         check_layer(Yh, X, W, s, "grouped wide rows M=%d K=%d g=%d" % (M, K, g))
         np.testing.assert_array_equal(Yh, host(tri.linear(Xd, Wps[g], s, K, F2)))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M", [4, 8, 16])
+def test_grouped_three_blocks_same_as_single(fmt, M):
+    """A group of 4096 and 7000 rows takes three 16-row blocks per workgroup (232 workgroups, one
+    round) while the 4096-row matrix alone takes one: the block count changes no arithmetic, so the
+    outputs are the oracle's within the bound and bitwise the same either way."""
+    import torch
+    K, Ns = 1000, [4096, 7000]
+    X = synth.activations(synth.rng_for(550 + fmt, M, synth.STREAM_X), M, K)
+    Ws = [synth.trits(synth.rng_for(550 + fmt, 10 * M + g, synth.STREAM_W), n, K) for g, n in enumerate(Ns)]
+    scales = [0.02, -0.03]
+    Xd = cuda(X)
+    Wps = [tri.pack(cuda(W), fmt) for W in Ws]
+    Ys = [torch.empty((M, n), dtype=torch.float16, device="cuda") for n in Ns]
+    say("grouped three blocks M=%d fmt=%d" % (M, fmt))
+    tri.tri_linear_grouped(Xd, Wps, scales, M, Ns, K, fmt, Ys)
+    for g, (W, s, Y) in enumerate(zip(Ws, scales, Ys)):
+        check_layer(host(Y), X, W, s, "grouped three blocks M=%d fmt=%d g=%d" % (M, fmt, g))
+    np.testing.assert_array_equal(host(Ys[0]), host(tri.linear(Xd, Wps[0], scales[0], K, fmt)))
