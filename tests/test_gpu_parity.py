@@ -478,26 +478,29 @@ def test_grouped_tall_matrices_same_as_single():
 # 2-bit tiles of 5..8 rows over rows of 8192 < K <= 12288 trits run on sixteen waves when the matrix
 # alone takes one 16-row block per workgroup; the choice is per matrix, so a group of such matrices
 # is one sixteen-wave launch and a mixed group one launch per matrix.
-WIDE16 = [(8, 11008, [4096, 3000]), (5, 9000, [4096, 3000]), (8, 11008, [4096, 6000]), (6, 9000, [6000, 4096])]
+# (1.6-bit: twelve waves, rows of 10240 < K <= 15360 trits.)
+WIDE16 = [(F2, 8, 11008, [4096, 3000]), (F2, 5, 9000, [4096, 3000]), (F2, 8, 11008, [4096, 6000]),
+          (F2, 6, 9000, [6000, 4096]), (F16, 8, 11008, [4096, 3000]), (F16, 7, 14000, [6000, 4096])]
 
 
-@pytest.mark.parametrize("M,K,Ns", WIDE16, ids=["M%dK%d_%d_%d" % (c[0], c[1], c[2][0], c[2][1]) for c in WIDE16])
-def test_grouped_wide_rows_same_as_single(M, K, Ns):
+@pytest.mark.parametrize("fmt,M,K,Ns", WIDE16,
+                         ids=["f%dM%dK%d_%d_%d" % (c[0], c[1], c[2], c[3][0], c[3][1]) for c in WIDE16])
+def test_grouped_wide_rows_same_as_single(fmt, M, K, Ns):
     """Every output against the oracle, and bitwise against the same matrix launched alone, for
-    groups whose matrices all take the sixteen-wave variant and for mixed groups."""
+    groups whose matrices all take the wide (sixteen- or twelve-wave) variant and for mixed groups."""
     import torch
     X = synth.activations(synth.rng_for(540, M, synth.STREAM_X), M, K)
     Ws = [synth.trits(synth.rng_for(540, 10 * M + g + Ns[g] % 97, synth.STREAM_W), n, K) for g, n in enumerate(Ns)]
     scales = [0.025, -0.04]
     Xd = cuda(X)
-    Wps = [tri.pack(cuda(W), F2) for W in Ws]
+    Wps = [tri.pack(cuda(W), fmt) for W in Ws]
     Ys = [torch.empty((M, n), dtype=torch.float16, device="cuda") for n in Ns]
-    say("grouped wide rows M=%d K=%d Ns=%s" % (M, K, Ns))
-    tri.tri_linear_grouped(Xd, Wps, scales, M, Ns, K, F2, Ys)
+    say("grouped wide rows fmt=%d M=%d K=%d Ns=%s" % (fmt, M, K, Ns))
+    tri.tri_linear_grouped(Xd, Wps, scales, M, Ns, K, fmt, Ys)
     for g, (W, s, Y) in enumerate(zip(Ws, scales, Ys)):
         Yh = host(Y)
-        check_layer(Yh, X, W, s, "grouped wide rows M=%d K=%d g=%d" % (M, K, g))
-        np.testing.assert_array_equal(Yh, host(tri.linear(Xd, Wps[g], s, K, F2)))
+        check_layer(Yh, X, W, s, "grouped wide rows fmt=%d M=%d K=%d g=%d" % (fmt, M, K, g))
+        np.testing.assert_array_equal(Yh, host(tri.linear(Xd, Wps[g], s, K, fmt)))
 
 
 @pytest.mark.parametrize("fmt", FMTS)
