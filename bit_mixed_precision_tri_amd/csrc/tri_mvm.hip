@@ -536,13 +536,13 @@ static bool launch_mt(const uint16_t *X, const Groups &gr, int M, int K, int C, 
 // eight-wave steps (8192 < K <= 12288; 1.6-bit: 10240 < K <= 15360), where the matrix alone would
 // run one block per workgroup and no glue but the residual applies: 11008 -> 4096 at M = 8
 // 7.76 -> 7.33 us (sixteen-row tiles gain nothing).  1.6-bit, whose sixteen-wave variants spill,
-// takes twelve waves of three or four steps: 11008 -> 4096 at M = 8 8.30 -> 8.03 us (sixteen-row
-// tiles: 9.80 -> 9.87 us, not used).  The wave count changes the order of the sums, so the choice is made per
+// takes twelve waves of three or four steps, for tiles of 3..8 rows: 11008 -> 4096 at M = 8
+// 8.30 -> 8.03 us, at M = 4 7.77 -> 7.58 us (sixteen-row tiles: 9.80 -> 9.87 us, not used).  The wave count changes the order of the sums, so the choice is made per
 // matrix: a group whose matrices all qualify runs as one such launch, a mixed group as one
 // launch per matrix, and every output stays bitwise equal to a single launch of its matrix.
 static bool wide16(const Groups &gr, int g, int M, int C, int fmt, const Fusion *fu)
 {
-    if (M < 5 || M > 8 || glue_bits(fu)) return false;
+    if (M < (fmt == TRI_FMT_2BIT ? 5 : 3) || M > 8 || glue_bits(fu)) return false;
     const int cst8 = (C + 31) / 32;
     if (cst8 < 5 || cst8 > 6) return false;
     const Groups one = make_groups(1, &gr.Wp[g], &gr.scale[g], &gr.N[g], &gr.Y[g]);
@@ -563,6 +563,9 @@ bool launch_mvm(const uint16_t *X, const Groups &gr, int M, int K, int fmt, hipS
     for (int g = 0; g < gr.G; ++g) n16 += wide16(gr, g, M, C, fmt, fu);
     if (n16 == gr.G) {
         if (fmt == TRI_FMT_2BIT) return launch_cfg<TRI_FMT_2BIT, 8, 16, 3>(X, gr, M, K, C, s, fu, 1);
+        if (M <= 4)
+            return (C + 47) / 48 <= 3 ? launch_cfg<TRI_FMT_1P6BIT, 4, 12, 3>(X, gr, M, K, C, s, fu, 1)
+                                      : launch_cfg<TRI_FMT_1P6BIT, 4, 12, 4>(X, gr, M, K, C, s, fu, 1);
         return (C + 47) / 48 <= 3 ? launch_cfg<TRI_FMT_1P6BIT, 8, 12, 3>(X, gr, M, K, C, s, fu, 1)
                                   : launch_cfg<TRI_FMT_1P6BIT, 8, 12, 4>(X, gr, M, K, C, s, fu, 1);
     }

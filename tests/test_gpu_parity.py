@@ -480,7 +480,8 @@ def test_grouped_tall_matrices_same_as_single():
 # is one sixteen-wave launch and a mixed group one launch per matrix.
 # (1.6-bit: twelve waves, rows of 10240 < K <= 15360 trits.)
 WIDE16 = [(F2, 8, 11008, [4096, 3000]), (F2, 5, 9000, [4096, 3000]), (F2, 8, 11008, [4096, 6000]),
-          (F2, 6, 9000, [6000, 4096]), (F16, 8, 11008, [4096, 3000]), (F16, 7, 14000, [6000, 4096])]
+          (F2, 6, 9000, [6000, 4096]), (F16, 8, 11008, [4096, 3000]), (F16, 7, 14000, [6000, 4096]),
+          (F16, 4, 11008, [4096, 3000]), (F16, 3, 14000, [6000, 4096])]
 
 
 @pytest.mark.parametrize("fmt,M,K,Ns", WIDE16,
